@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse latent-attention prefill on one MI355X.
+
+One step = the whole hot path on one batch of seeded synthetic inputs already resident in HBM:
+mla_kv_latent (down-projection + RMSNorm + rotary), mla_kv_up (up-projection) and
+mla_sparse_prefill_attn (selection bitmap + sparse attention), all on one stream.
+Default workload: B=2, T=4096, top-k 2048, 128 heads (the headline prefill shape).
+
+Prints one JSON line. `value` is tokens/s of the whole path (B*T tokens per step). `roofline`
+prices the dominant call (the attention) at its algorithmic work: 640 FLOP per selected
+(query, head, key) = 2*192 for q.k plus 2*128 for p.v, against the bf16 dense MFMA peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+METRIC = "MLA sparse-prefill tokens/s + % bf16 MFMA peak (T=4096, top-k 2048)"
+
+
+def selected_pairs(topk: np.ndarray) -> int:
+    """Number of (b, s, t) with t selected for query s and t <= s (set semantics)."""
+    B, T, K = topk.shape
+    n = 0
+    s = np.arange(T)[:, None]
+    for b in range(B):
+        t = topk[b].astype(np.int64)
+        ok = (t >= 0) & (t <= s)
+        # distinct entries per row
+        key = np.where(ok, t, -1)
+        key.sort(axis=1)
+        distinct = ok.sum(1) - ((key[:, 1:] == key[:, :-1]) & (key[:, 1:] >= 0)).sum(1)
+        n += int(distinct.sum())
+    return n
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the record matches the current
+    kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    src = os.path.join(ROOT, "sparse_latent_attention_wkv_amd", "csrc", "attn.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("source_sha") != sha or "bytes_per_launch" not in kv:
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+def cpu_baseline(d: dict, B: int, T: int, heads_sample: int) -> dict:
+    """Time the CPU oracle on batch 0: the front end and up-projection for all of its tokens,
+    the attention for `heads_sample` of its 128 heads; scale linearly to the whole workload."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # noqa: BLE001
+        cores = 1
+    f32 = synth.bf16_bits_to_f32
+    x = f32(d["x"][:1])
+    t0 = time.perf_counter()
+    kv_raw, c_kv, k_pe = oracle.kv_latent(x, f32(d["w_dkv"]), d["gain"])
+    t1 = time.perf_counter()
+    kv = oracle.kv_up(c_kv, f32(d["w_ukv"]))
+    t2 = time.perf_counter()
+    q = f32(d["q"][:1])
+    oracle.sparse_prefill_attn(q, kv, k_pe, d["topk"][:1], oracle.softmax_scale(),
+                               heads=range(heads_sample))
+    t3 = time.perf_counter()
+    per_batch = (t1 - t0) + (t2 - t1) + (t3 - t2) * (128 / heads_sample)
+    total = per_batch * B
+    return {"value": B * T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"batch 0 of {B}: front end + up-projection for all {T} tokens "
+                       f"({t1 - t0:.1f} s + {t2 - t1:.1f} s), dense-masked attention for "
+                       f"{heads_sample} of 128 heads ({t3 - t2:.1f} s); scaled linearly to "
+                       f"{B} batches x 128 heads. float64 NumPy; BLAS threads = cores, "
+                       f"elementwise single-threaded"),
+            "sample_seconds": round(t3 - t0, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline", choices=["headline", "1k", "long", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU runs are not supported by this build", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import synth
+    import sparse_latent_attention_wkv_amd as mla
+
+    w = synth.WORKLOADS[args.workload]
+    B, T, K = w.B, w.T, w.K
+    t_gen = time.perf_counter()
+    d = synth.make(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w_dkv, w_ukv, q = up(d["x"]), up(d["w_dkv"]), up(d["w_ukv"]), up(d["q"])
+    gain = torch.from_numpy(d["gain"]).to(dev)
+    topk = torch.from_numpy(d["topk"]).to(dev)
+    rope_cs = mla.mla_rope_table(T, dev)           # the model's freqs_cis: built once
+    kv_raw = torch.empty((B, T, 576), dtype=torch.bfloat16, device=dev)
+    c_kv = torch.empty((B, T, 512), dtype=torch.bfloat16, device=dev)
+    k_pe = torch.empty((B, T, 64), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((B, 128, T, 256), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_attn_workspace_bytes(B, T, K), dtype=torch.uint8, device=dev)
+    scale = mla.mla_default_softmax_scale()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_kv_latent(x, w_dkv, gain, 1e-6, rope_cs, out=(kv_raw, c_kv, k_pe))
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_kv_up(c_kv, w_ukv, out=kv)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.mla_sparse_prefill_attn(q, kv, k_pe, topk, scale, workspace=ws, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    upm = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    att = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs = selected_pairs(d["topk"])
+    attn_flop = 640.0 * pairs * 128
+    causal_pairs = B * T * (T + 1) // 2
+    achieved = attn_flop / (att * 1e-3) / 1e12
+    flop_down = 2.0 * B * T * 7168 * 576
+    flop_up = 2.0 * B * T * 512 * 32768
+    tokens = B * T
+    traffic = traffic_record("sparse_attn")
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"sparse MLA prefill {args.workload}: B={B}, T={T}, top-k {K}, "
+                               "128 heads, qk 192 / v 128, hidden 7168, latent 512+64",
+                   "B": B, "T": T, "top_k": K, "heads": 128, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "mla_sparse_prefill_attn call (sel_bitmap + sparse_attn kernels)",
+                     "algorithmic_flop_per_launch": attn_flop},
+        "stages_ms": {"kv_latent": lat, "kv_up": upm, "sparse_attn": att, "gpu_step": gpu_step},
+        "stage_tflops": {"kv_latent": flop_down / (lat * 1e-3) / 1e12,
+                         "kv_up": flop_up / (upm * 1e-3) / 1e12},
+        "selected_pairs_all_batches": pairs,
+        "scored_over_selected_upper_bound": causal_pairs / pairs,
+        "input_generation_s": round(t_gen, 2),
+    }
+    if rank == 0 and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, B, T, min(args.cpu_heads, 128))
+    if rank == 0:
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) sparse latent-attention prefill library (libmla.so).
+ *
+ * The library computes the DeepSeek-V3.2-Exp sparse multi-head latent-attention prefill as the
+ * model-atlas pages describe it:
+ *
+ *   mla_kv_latent            x -> joint KV down-projection (512 latent + 64 rotary key),
+ *                            fp32 RMSNorm of the latent, rotary rotation of the shared key
+ *                            ("DeepSeek-V3.2-Exp · Key-value down-projection": formula and the
+ *                            MLA key-value code excerpt; "DeepSeek V4.1 · Key-value RMSNorm":
+ *                            formula and the RMSNorm code excerpt).
+ *   mla_kv_up                latent -> 128 heads of [128 non-rotary key | 128 value]
+ *                            ("DeepSeek-V3.2-Exp · Keys": MHA-prefill code excerpt;
+ *                            "DeepSeek-V3.2-Exp · Split value heads": [B,T,16384] -> [B,128,T,128]).
+ *   mla_sparse_prefill_attn  scores over [k_nope | k_pe] times the softmax scale, restricted to
+ *                            the top-k selection intersected with the causal mask, softmax over
+ *                            keys, value mixing ("DeepSeek-V3.2-Exp · Keys": MHA-prefill code
+ *                            excerpt; "DeepSeek-V3.2-Exp · Scale scores": formula).
+ *
+ * Conventions for every call
+ *  - Pointers marked (device) are HIP device pointers; all tensors are dense, row-major,
+ *    contiguous, and must be 16-byte aligned. bf16 tensors are passed as raw 16-bit storage.
+ *  - The caller owns every buffer (inputs, outputs, workspace). The library allocates no memory
+ *    and keeps no state beyond a per-device architecture check.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue
+ *    work on it and return; nothing is synchronised. Device faults surface at the caller's next
+ *    synchronisation.
+ *  - Return value: MLA_OK (0) or a negative MLA_E_* code. On a negative code nothing was
+ *    enqueued. Argument checks run before any HIP call. MLA_E_LAUNCH reports a HIP launch
+ *    failure; mla_last_hip_error() then returns the hipError_t of this thread's last failure.
+ *  - Outputs must not overlap inputs.
+ *  - Model dimensions are fixed at compile time (the MLA constructor excerpt and the pages'
+ *    shapes): hidden 7168, latent 512, rotary 64, 128 heads, 192 = 128 + 64 query/key features,
+ *    128 value features.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_HIDDEN 7168
+#define MLA_KV_LORA 512
+#define MLA_ROPE 64
+#define MLA_KV_A_OUT 576      /* MLA_KV_LORA + MLA_ROPE rows of the down-projection weight */
+#define MLA_HEADS 128
+#define MLA_QK_NOPE 128
+#define MLA_QK_HEAD 192       /* MLA_QK_NOPE + MLA_ROPE */
+#define MLA_V_HEAD 128
+#define MLA_KV_B_OUT 32768    /* MLA_HEADS * (MLA_QK_NOPE + MLA_V_HEAD) */
+#define MLA_MAX_T 32768       /* longest sequence the selection/attention calls accept */
+#define MLA_MAX_ROWS (1 << 24)
+
+enum {
+    MLA_OK = 0,
+    MLA_E_NULL = -1,       /* a required pointer is NULL */
+    MLA_E_SHAPE = -2,      /* B, T, K, rows or a stride outside the supported range */
+    MLA_E_ALIGN = -3,      /* a pointer is not 16-byte aligned */
+    MLA_E_WORKSPACE = -4,  /* workspace smaller than mla_attn_workspace_bytes() */
+    MLA_E_DEVICE = -5,     /* current device is not gfx950, or no device */
+    MLA_E_LAUNCH = -6,     /* a kernel launch failed (see mla_last_hip_error) */
+    MLA_E_ARG = -7,        /* eps, theta or softmax_scale not finite and > 0 */
+    MLA_E_ALIAS = -8       /* an output overlaps an input or another output */
+};
+
+/*
+ * Joint KV down-projection, latent RMSNorm and rotary key (one call for the front end).
+ *   x        (device) bf16 [B, T, 7168]
+ *   w_dkv    (device) bf16 [576, 7168], stored [out, in] as the Linear excerpt holds weights;
+ *            rows 0..511 produce the latent, rows 512..575 the shared rotary key.
+ *   kv_gain  (device) fp32 [512], the RMSNorm learned gain.
+ *   eps      RMSNorm epsilon (1e-6 is the RMSNorm class default used by the V3.2 kv_norm).
+ *   rope_cs  (device) fp32 [T, 32, 2]: (cos, sin) of t * theta^(-2i/64) for t < T, i < 32
+ *            (the pages' freqs_cis; build it with mla_rope_table).
+ *   kv_raw   (device, out) bf16 [B, T, 576], the down-projection output (fp32 accumulation,
+ *            one rounding to bf16).
+ *   c_kv     (device, out) bf16 [B, T, 512] = bf16(gain * x / sqrt(mean(x^2) + eps)), computed in
+ *            fp32 from kv_raw[..., :512].
+ *   k_pe     (device, out) bf16 [B, T, 64]: kv_raw[..., 512:] with pairs (2i, 2i+1) rotated as
+ *            complex numbers by angle t * theta^(-2i/64), fp32 arithmetic.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (B, T < 1, B*T > MLA_MAX_ROWS), MLA_E_ALIGN, MLA_E_ARG,
+ *         MLA_E_ALIAS, MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_kv_latent(const void* x, const void* w_dkv, const float* kv_gain, float eps,
+                  const float* rope_cs, int B, int T, void* kv_raw, void* c_kv, void* k_pe,
+                  void* stream);
+
+/*
+ * The norm/rotary step alone (the second half of mla_kv_latent), also used for the V4.1
+ * window-KV decode norm ("DeepSeek V4.1 · Key-value RMSNorm": eps = 1e-20, in/out [B, 1, 512]).
+ *   kv_raw      (device) bf16 [rows, row_stride]; row_stride is 576 (latent + rotary key) or
+ *               512 (latent only).
+ *   has_rope    nonzero: rotate kv_raw[r, 512:576] into k_pe[r] at position r % T (requires
+ *               row_stride 576, rope_cs and k_pe); zero: no rotary output (rope_cs, k_pe, T unused).
+ *   gain, eps   as for mla_kv_latent.
+ *   c_kv        (device, out) bf16 [rows, 512];  k_pe (device, out) bf16 [rows, 64].
+ * Errors: as mla_kv_latent.
+ */
+int mla_kv_norm_rope(const void* kv_raw, int rows, int row_stride, int has_rope,
+                     const float* gain, float eps, const float* rope_cs, int T, void* c_kv,
+                     void* k_pe, void* stream);
+
+/*
+ * Rotary table for positions 0..T-1: rope_cs[t][i] = (cos, sin)(t * theta^(-2i/64)), i < 32,
+ * evaluated in fp64 on the device and rounded to fp32 (the pages pass this table, freqs_cis,
+ * into the rotary helper; the model-args excerpt sets rope_theta = 10000).
+ *   rope_cs (device, out) fp32 [T, 32, 2].
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (T < 1 or T > MLA_MAX_ROWS), MLA_E_ARG, MLA_E_DEVICE,
+ *         MLA_E_LAUNCH.
+ */
+int mla_rope_table(int T, float theta, float* rope_cs, void* stream);
+
+/*
+ * KV up-projection into head-major keys and values.
+ *   c_kv   (device) bf16 [B, T, 512]
+ *   w_ukv  (device) bf16 [32768, 512], [out, in]; output feature h*256 + j is head h's
+ *          non-rotary key feature j for j < 128 and its value feature j - 128 otherwise.
+ *   kv     (device, out) bf16 [B, 128, T, 256]: kv[b, h, t, :] = bf16(c_kv[b, t] . W[h*256 : h*256+256]^T)
+ *          with fp32 accumulation.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_ALIAS, MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_kv_up(const void* c_kv, const void* w_ukv, int B, int T, void* kv, void* stream);
+
+/*
+ * Bytes of workspace mla_sparse_prefill_attn needs (the selection bitmap, 4 * B * ceil(T/32) * T
+ * bytes, rounded up to 256). Returns 0 for shapes the call would reject.
+ */
+size_t mla_attn_workspace_bytes(int B, int T, int K);
+
+/*
+ * Selection intersected with the causal mask, as a bitmap (the MHA-prefill excerpt's scattered
+ * index mask plus causal mask, stored as bits).
+ *   topk    (device) int32 [B, T, K]: key positions per query. Entries outside [0, T) select
+ *           nothing (-1 marks an empty slot); repeated entries select once; entries > s are
+ *           removed by the causal mask.
+ *   bitmap  (device, out) uint32 [B, ceil(T/32), T]: bit (t % 32) of bitmap[b][t / 32][s] is
+ *           set iff t is one of row s's entries and t <= s.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (B, T, K < 1, T > MLA_MAX_T, K > 65536), MLA_E_ALIGN,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap, void* stream);
+
+/*
+ * Sparse prefill attention.
+ *   q        (device) bf16 [B, T, 128, 192], each head's query as [128 non-rotary | 64 rotary]
+ *            (the excerpt concatenates q_nope and q_pe in that order).
+ *   kv       (device) bf16 [B, 128, T, 256] from mla_kv_up.
+ *   k_pe     (device) bf16 [B, T, 64], shared by all heads (appended to every head's key).
+ *   topk     (device) int32 [B, T, K], as for mla_selection_bitmap.
+ *   softmax_scale  multiplies q.k (mla_default_softmax_scale() gives m^2/sqrt(192)).
+ *   out      (device, out) bf16 [B, T, 128, 128]:
+ *            out[b,s,h] = sum_{t in A(b,s)} softmax_t(scale * q[b,s,h] . k[b,h,t]) v[b,h,t],
+ *            fp32 scores, softmax and accumulation; A(b,s) = selected keys with t <= s.
+ *            Keys outside A(b,s) receive exactly zero weight.
+ *   workspace, ws_bytes  (device) scratch of at least mla_attn_workspace_bytes(B, T, K) bytes;
+ *            its contents on entry do not matter and are overwritten.
+ * Precondition (not checked): every query has at least one allowed key (the workloads always
+ * select the query's own position); an empty row yields NaN, as the pages' form does.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ARG, MLA_E_ALIAS,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
+                            int B, int T, int K, float softmax_scale, void* out, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* m^2 / sqrt(192) with m = 1 + 0.1 ln 40, rounded to fp32 ("DeepSeek-V3.2-Exp · Scale scores"). */
+float mla_default_softmax_scale(void);
+
+/* Static string naming a status code. */
+const char* mla_status_string(int status);
+
+/* hipError_t of this thread's last failed HIP call inside the library (0 if none). */
+int mla_last_hip_error(void);
+
+/* Static string describing the build (target architecture, compiler). */
+const char* mla_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,206 @@
+"""MI355X (gfx950) sparse latent-attention prefill: Python binding of libmla.so.
+
+The functions below carry the names of the C entry points in ``include/mla.h`` and only
+marshal arguments: they check dtypes, shapes, devices and contiguity of torch tensors, allocate
+outputs with ``torch.empty`` on the input's device, and call the library on the current torch
+stream. Every step of the computation runs in the library's HIP kernels; there is no fallback.
+If ``libmla.so`` has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+HIDDEN, KV_LORA, ROPE, KV_A_OUT = 7168, 512, 64, 576
+HEADS, QK_NOPE, QK_HEAD, V_HEAD = 128, 128, 192, 128
+KV_B_OUT = HEADS * (QK_NOPE + V_HEAD)
+
+_lib = None
+
+_VP, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "mla_kv_latent": (_I, [_VP, _VP, _VP, _F, _VP, _I, _I, _VP, _VP, _VP, _VP]),
+    "mla_kv_norm_rope": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _VP, _VP, _VP]),
+    "mla_rope_table": (_I, [_I, _F, _VP, _VP]),
+    "mla_kv_up": (_I, [_VP, _VP, _I, _I, _VP, _VP]),
+    "mla_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "mla_selection_bitmap": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "mla_sparse_prefill_attn": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP, _SZ, _VP]),
+    "mla_default_softmax_scale": (_F, []),
+    "mla_status_string": (ctypes.c_char_p, [_I]),
+    "mla_last_hip_error": (_I, []),
+    "mla_build_info": (ctypes.c_char_p, []),
+}
+
+
+class MLAError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MLAError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_latent_attention_wkv_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().mla_status_string(status).decode()
+        if status == -6:
+            msg += f" (hipError {lib().mla_last_hip_error()})"
+        raise MLAError(msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def mla_default_softmax_scale() -> float:
+    return float(lib().mla_default_softmax_scale())
+
+
+def mla_attn_workspace_bytes(B: int, T: int, K: int) -> int:
+    return int(lib().mla_attn_workspace_bytes(B, T, K))
+
+
+def mla_rope_table(T: int, device, theta: float = 10000.0) -> torch.Tensor:
+    """(cos, sin) table [T, 32, 2] fp32 for positions 0..T-1."""
+    out = torch.empty((T, 32, 2), dtype=torch.float32, device=device)
+    with torch.cuda.device(out.device):
+        _check(lib().mla_rope_table(T, theta, _ptr(out), _stream(out.device)))
+    return out
+
+
+def mla_kv_latent(x, w_dkv, kv_gain, eps: float = 1e-6, rope_cs=None, out=None):
+    """x [B, T, 7168] bf16 -> (kv_raw [B, T, 576], c_kv [B, T, 512], k_pe [B, T, 64]) bf16."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, 7168]")
+    B, T, _ = x.shape
+    _need(x, "x", torch.bfloat16, (B, T, HIDDEN))
+    _need(w_dkv, "w_dkv", torch.bfloat16, (KV_A_OUT, HIDDEN))
+    _need(kv_gain, "kv_gain", torch.float32, (KV_LORA,))
+    if rope_cs is None:
+        rope_cs = mla_rope_table(T, x.device)
+    _need(rope_cs, "rope_cs", torch.float32, (T, 32, 2))
+    if out is None:
+        out = (torch.empty((B, T, KV_A_OUT), dtype=torch.bfloat16, device=x.device),
+               torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=x.device),
+               torch.empty((B, T, ROPE), dtype=torch.bfloat16, device=x.device))
+    kv_raw, c_kv, k_pe = out
+    with torch.cuda.device(x.device):
+        _check(lib().mla_kv_latent(_ptr(x), _ptr(w_dkv), _ptr(kv_gain), eps, _ptr(rope_cs), B, T,
+                                   _ptr(kv_raw), _ptr(c_kv), _ptr(k_pe), _stream(x.device)))
+    return kv_raw, c_kv, k_pe
+
+
+def mla_kv_norm_rope(kv_raw, gain, eps: float = 1e-6, rope_cs=None, T: int | None = None):
+    """kv_raw [rows, 576] (latent + rotary key) or [rows, 512] (latent only) bf16 ->
+    (c_kv [rows, 512], k_pe [rows, 64] or None). Row r is at position r % T for the rotary."""
+    if kv_raw.dim() != 2:
+        raise ValueError("kv_raw must be 2-D [rows, 576 or 512]")
+    rows, stride = kv_raw.shape
+    _need(kv_raw, "kv_raw", torch.bfloat16)
+    _need(gain, "gain", torch.float32, (KV_LORA,))
+    has_rope = rope_cs is not None
+    c_kv = torch.empty((rows, KV_LORA), dtype=torch.bfloat16, device=kv_raw.device)
+    k_pe = None
+    if has_rope:
+        T = rope_cs.shape[0] if T is None else T
+        _need(rope_cs, "rope_cs", torch.float32, (T, 32, 2))
+        k_pe = torch.empty((rows, ROPE), dtype=torch.bfloat16, device=kv_raw.device)
+    with torch.cuda.device(kv_raw.device):
+        _check(lib().mla_kv_norm_rope(_ptr(kv_raw), rows, stride, int(has_rope), _ptr(gain), eps,
+                                      _ptr(rope_cs), T or 1, _ptr(c_kv), _ptr(k_pe),
+                                      _stream(kv_raw.device)))
+    return c_kv, k_pe
+
+
+def mla_kv_up(c_kv, w_ukv, out=None):
+    """c_kv [B, T, 512] bf16 -> kv [B, 128, T, 256] bf16 (per head: 128 key | 128 value)."""
+    if c_kv.dim() != 3:
+        raise ValueError("c_kv must be [B, T, 512]")
+    B, T, _ = c_kv.shape
+    _need(c_kv, "c_kv", torch.bfloat16, (B, T, KV_LORA))
+    _need(w_ukv, "w_ukv", torch.bfloat16, (KV_B_OUT, KV_LORA))
+    if out is None:
+        out = torch.empty((B, HEADS, T, QK_NOPE + V_HEAD), dtype=torch.bfloat16, device=c_kv.device)
+    _need(out, "out", torch.bfloat16, (B, HEADS, T, QK_NOPE + V_HEAD))
+    with torch.cuda.device(c_kv.device):
+        _check(lib().mla_kv_up(_ptr(c_kv), _ptr(w_ukv), B, T, _ptr(out), _stream(c_kv.device)))
+    return out
+
+
+def mla_selection_bitmap(topk):
+    """topk [B, T, K] int32 -> bitmap [B, ceil(T/32), T] int32 (bit t%32 of word t/32 of row s)."""
+    if topk.dim() != 3:
+        raise ValueError("topk must be [B, T, K]")
+    B, T, K = topk.shape
+    _need(topk, "topk", torch.int32)
+    bm = torch.empty((B, (T + 31) // 32, T), dtype=torch.int32, device=topk.device)
+    with torch.cuda.device(topk.device):
+        _check(lib().mla_selection_bitmap(_ptr(topk), B, T, K, _ptr(bm), _stream(topk.device)))
+    return bm
+
+
+def mla_sparse_prefill_attn(q, kv, k_pe, topk, softmax_scale: float | None = None,
+                            workspace=None, out=None):
+    """q [B, T, 128, 192], kv [B, 128, T, 256], k_pe [B, T, 64] bf16, topk [B, T, K] int32 ->
+    out [B, T, 128, 128] bf16."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, 128, 192]")
+    B, T = q.shape[0], q.shape[1]
+    _need(q, "q", torch.bfloat16, (B, T, HEADS, QK_HEAD))
+    _need(kv, "kv", torch.bfloat16, (B, HEADS, T, QK_NOPE + V_HEAD))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
+    if topk.dim() != 3 or topk.shape[:2] != (B, T):
+        raise ValueError("topk must be [B, T, K]")
+    _need(topk, "topk", torch.int32)
+    K = topk.shape[2]
+    if softmax_scale is None:
+        softmax_scale = mla_default_softmax_scale()
+    need = mla_attn_workspace_bytes(B, T, K)
+    if need == 0:
+        raise MLAError("unsupported attention shape")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, HEADS, V_HEAD), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, HEADS, V_HEAD))
+    with torch.cuda.device(q.device):
+        _check(lib().mla_sparse_prefill_attn(_ptr(q), _ptr(kv), _ptr(k_pe), _ptr(topk), B, T, K,
+                                             softmax_scale, _ptr(out), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(q.device)))
+    return out

@@ -1,0 +1,246 @@
+// C ABI of libmla.so (declared in include/mla.h): argument validation, the device check and the
+// kernel sequence of each call. Validation happens before any HIP call, so a rejected call has
+// no side effects.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/mla.h"
+#include "mla_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// True if any output overlaps any other span (inputs or outputs).
+bool any_alias(const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+bool pos_finite(float v) { return isfinite(v) && v > 0.f; }
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        g_last_hip_error = (int)e;
+        return MLA_E_DEVICE;
+    }
+    if (dev < kMaxDevices) {
+        const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (c == 1) return MLA_OK;
+        if (c == 2) return MLA_E_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MLA_E_DEVICE;
+    }
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MLA_OK : MLA_E_DEVICE;
+}
+
+int launched(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MLA_E_LAUNCH;
+    }
+    return MLA_OK;
+}
+
+constexpr size_t kBf16 = 2;
+
+int validate_norm_rope(const void* kv_raw, int rows, int row_stride, int has_rope, const float* gain,
+                       float eps, const float* rope_cs, int T, const void* c_kv, const void* k_pe) {
+    if (!kv_raw || !gain || !c_kv) return MLA_E_NULL;
+    if (has_rope && (!rope_cs || !k_pe)) return MLA_E_NULL;
+    if (rows < 1 || rows > MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (row_stride != MLA_KV_A_OUT && row_stride != MLA_KV_LORA) return MLA_E_SHAPE;
+    if (has_rope && (row_stride != MLA_KV_A_OUT || T < 1 || T > MLA_MAX_ROWS)) return MLA_E_SHAPE;
+    if (!aligned16(kv_raw) || !aligned16(gain) || !aligned16(c_kv)) return MLA_E_ALIGN;
+    if (has_rope && (!aligned16(rope_cs) || !aligned16(k_pe))) return MLA_E_ALIGN;
+    if (!pos_finite(eps)) return MLA_E_ARG;
+    const Span ins[] = {{kv_raw, (size_t)rows * row_stride * kBf16},
+                        {gain, MLA_KV_LORA * sizeof(float)},
+                        {rope_cs, has_rope ? (size_t)T * 64 * sizeof(float) : 0}};
+    const Span outs[] = {{c_kv, (size_t)rows * MLA_KV_LORA * kBf16},
+                         {k_pe, has_rope ? (size_t)rows * MLA_ROPE * kBf16 : 0}};
+    if (any_alias(outs, 2, ins, 3)) return MLA_E_ALIAS;
+    return MLA_OK;
+}
+
+int validate_topk(const int32_t* topk, int B, int T, int K) {
+    if (!topk) return MLA_E_NULL;
+    if (B < 1 || T < 1 || K < 1 || T > MLA_MAX_T || K > 65536) return MLA_E_SHAPE;
+    if ((size_t)B * T > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(topk)) return MLA_E_ALIGN;
+    return MLA_OK;
+}
+
+size_t bitmap_bytes(int B, int T) { return (size_t)B * ((T + 31) / 32) * T * sizeof(uint32_t); }
+
+}  // namespace
+
+extern "C" {
+
+int mla_kv_norm_rope(const void* kv_raw, int rows, int row_stride, int has_rope, const float* gain,
+                     float eps, const float* rope_cs, int T, void* c_kv, void* k_pe, void* stream) {
+    int st = validate_norm_rope(kv_raw, rows, row_stride, has_rope, gain, eps, rope_cs, T, c_kv, k_pe);
+    if (st != MLA_OK) return st;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_norm_rope(static_cast<const uint16_t*>(kv_raw), rows, row_stride,
+                                          has_rope != 0, gain, eps, rope_cs, has_rope ? T : 1,
+                                          static_cast<uint16_t*>(c_kv), static_cast<uint16_t*>(k_pe),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int mla_kv_latent(const void* x, const void* w_dkv, const float* kv_gain, float eps,
+                  const float* rope_cs, int B, int T, void* kv_raw, void* c_kv, void* k_pe,
+                  void* stream) {
+    if (!x || !w_dkv || !kv_gain || !rope_cs || !kv_raw || !c_kv || !k_pe) return MLA_E_NULL;
+    if (B < 1 || T < 1 || (size_t)B * T > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(kv_gain) || !aligned16(rope_cs) ||
+        !aligned16(kv_raw) || !aligned16(c_kv) || !aligned16(k_pe))
+        return MLA_E_ALIGN;
+    if (!pos_finite(eps)) return MLA_E_ARG;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{x, M * MLA_HIDDEN * kBf16},
+                        {w_dkv, (size_t)MLA_KV_A_OUT * MLA_HIDDEN * kBf16},
+                        {kv_gain, MLA_KV_LORA * sizeof(float)},
+                        {rope_cs, (size_t)T * 64 * sizeof(float)}};
+    const Span outs[] = {{kv_raw, M * MLA_KV_A_OUT * kBf16},
+                         {c_kv, M * MLA_KV_LORA * kBf16},
+                         {k_pe, M * MLA_ROPE * kBf16}};
+    if (any_alias(outs, 3, ins, 4)) return MLA_E_ALIAS;
+    int st = check_device();
+    if (st != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(mla::launch_gemm_kv_down(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(w_dkv), (int)M,
+                                           static_cast<uint16_t*>(kv_raw), s));
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_norm_rope(static_cast<const uint16_t*>(kv_raw), (int)M, MLA_KV_A_OUT,
+                                          true, kv_gain, eps, rope_cs, T, static_cast<uint16_t*>(c_kv),
+                                          static_cast<uint16_t*>(k_pe), s));
+}
+
+int mla_rope_table(int T, float theta, float* rope_cs, void* stream) {
+    if (!rope_cs) return MLA_E_NULL;
+    if (T < 1 || T > MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(rope_cs)) return MLA_E_ALIGN;
+    if (!pos_finite(theta)) return MLA_E_ARG;
+    int st = check_device();
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_rope_table(T, (double)theta, rope_cs, static_cast<hipStream_t>(stream)));
+}
+
+int mla_kv_up(const void* c_kv, const void* w_ukv, int B, int T, void* kv, void* stream) {
+    if (!c_kv || !w_ukv || !kv) return MLA_E_NULL;
+    if (B < 1 || T < 1 || (size_t)B * T > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(c_kv) || !aligned16(w_ukv) || !aligned16(kv)) return MLA_E_ALIGN;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{c_kv, M * MLA_KV_LORA * kBf16}, {w_ukv, (size_t)MLA_KV_B_OUT * MLA_KV_LORA * kBf16}};
+    const Span outs[] = {{kv, M * MLA_KV_B_OUT * kBf16}};
+    if (any_alias(outs, 1, ins, 2)) return MLA_E_ALIAS;
+    int st = check_device();
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_gemm_kv_up(static_cast<const uint16_t*>(c_kv),
+                                           static_cast<const uint16_t*>(w_ukv), B, T,
+                                           static_cast<uint16_t*>(kv), static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_attn_workspace_bytes(int B, int T, int K) {
+    if (validate_topk(reinterpret_cast<const int32_t*>(16), B, T, K) != MLA_OK) return 0;
+    return (bitmap_bytes(B, T) + 255) & ~(size_t)255;
+}
+
+int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap, void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!bitmap) return MLA_E_NULL;
+    if (!aligned16(bitmap)) return MLA_E_ALIGN;
+    const Span ins[] = {{topk, (size_t)B * T * K * sizeof(int32_t)}};
+    const Span outs[] = {{bitmap, bitmap_bytes(B, T)}};
+    if (any_alias(outs, 1, ins, 1)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_sel_bitmap(topk, B, T, K, bitmap, static_cast<hipStream_t>(stream)));
+}
+
+int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
+                            int B, int T, int K, float softmax_scale, void* out, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!q || !kv || !k_pe || !out || !workspace) return MLA_E_NULL;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(k_pe) || !aligned16(out) || !aligned16(workspace))
+        return MLA_E_ALIGN;
+    if (!pos_finite(softmax_scale)) return MLA_E_ARG;
+    if (ws_bytes < bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
+                        {kv, M * MLA_HEADS * 256 * kBf16},
+                        {k_pe, M * MLA_ROPE * kBf16},
+                        {topk, M * K * sizeof(int32_t)}};
+    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}, {workspace, bitmap_bytes(B, T)}};
+    if (any_alias(outs, 2, ins, 4)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* bm = static_cast<uint32_t*>(workspace);
+    st = launched(mla::launch_sel_bitmap(topk, B, T, K, bm, s));
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
+                                            static_cast<const uint16_t*>(kv),
+                                            static_cast<const uint16_t*>(k_pe), bm, B, T,
+                                            softmax_scale, static_cast<uint16_t*>(out), s));
+}
+
+float mla_default_softmax_scale(void) {
+    const double m = 1.0 + 0.1 * log(40.0);
+    return (float)(m * m / sqrt(192.0));
+}
+
+const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_E_NULL: return "MLA_E_NULL: a required pointer is NULL";
+        case MLA_E_SHAPE: return "MLA_E_SHAPE: unsupported shape";
+        case MLA_E_ALIGN: return "MLA_E_ALIGN: pointer not 16-byte aligned";
+        case MLA_E_WORKSPACE: return "MLA_E_WORKSPACE: workspace too small";
+        case MLA_E_DEVICE: return "MLA_E_DEVICE: current device is not gfx950";
+        case MLA_E_LAUNCH: return "MLA_E_LAUNCH: kernel launch failed";
+        case MLA_E_ARG: return "MLA_E_ARG: eps/theta/scale must be finite and positive";
+        case MLA_E_ALIAS: return "MLA_E_ALIAS: an output overlaps another buffer";
+        default: return "unknown status";
+    }
+}
+
+int mla_last_hip_error(void) { return g_last_hip_error; }
+
+const char* mla_build_info(void) { return "libmla gfx950 (hipcc " __clang_version__ ")"; }
+
+}  // extern "C"

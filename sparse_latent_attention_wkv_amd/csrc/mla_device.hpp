@@ -1,0 +1,65 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16 packing, MFMA wrappers
+// and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHidden = 7168;
+constexpr int kLora = 512;
+constexpr int kRope = 64;
+constexpr int kKvAOut = 576;
+constexpr int kHeads = 128;
+constexpr int kNope = 128;
+constexpr int kQkHead = 192;
+constexpr int kVHead = 128;
+constexpr int kKvBOut = 32768;
+
+// bf16 storage <-> fp32 (exact widening).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two fp32 values to bf16 (nearest, ties to even; the gfx950 conversion instruction) and
+// pack them, `lo` in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Operand layout (wave64): lane l supplies row/column
+// (l % 32) and eight consecutive reduction indices selected by (l / 32); the 16 results of
+// lane l are D[8*(r/4) + 4*(l/32) + (r%4)][l % 32], r = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) { return *p; }
+
+// Non-temporal-free plain 16-byte global load / store.
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void store8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace mla

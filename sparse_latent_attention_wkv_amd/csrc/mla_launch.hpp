@@ -1,0 +1,24 @@
+// Host-side launchers of the gfx950 kernels (internal to libmla.so; the C ABI in include/mla.h
+// validates arguments and then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+hipError_t launch_norm_rope(const uint16_t* src, int rows, int stride, bool rope, const float* gain,
+                            float eps, const float* rope_cs, int T, uint16_t* c_kv, uint16_t* k_pe,
+                            hipStream_t stream);
+hipError_t launch_rope_table(int T, double theta, float* rope_cs, hipStream_t stream);
+hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, uint16_t* kv_raw,
+                               hipStream_t stream);
+hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
+                             hipStream_t stream);
+hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap,
+                             hipStream_t stream);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint16_t* k_pe,
+                              const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
+                              hipStream_t stream);
+
+}  // namespace mla

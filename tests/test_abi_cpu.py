@@ -1,0 +1,132 @@
+"""The C ABI on the host: libmla.so loads, exports every function include/mla.h declares, and
+rejects bad arguments before any HIP call (no GPU needed; no kernel is launched here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("sparse_latent_attention_wkv_amd")
+
+
+def _lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.fail("libmla.so is not built (run __graft_entry__.build())")
+    return mla.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_path_calls():
+    names = declared_functions()
+    for n in ("mla_kv_latent", "mla_kv_up", "mla_sparse_prefill_attn"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in mla._SIGS, f"binding does not declare {name}"
+
+
+def test_host_only_helpers():
+    lib = _lib()
+    s = lib.mla_default_softmax_scale()
+    m = 1 + 0.1 * math.log(40)
+    assert s == pytest.approx(m * m / math.sqrt(192), rel=1e-7)
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    for code in range(-8, 0):
+        assert lib.mla_status_string(code).startswith(b"MLA_E_")
+    assert b"gfx950" in lib.mla_build_info()
+    # bitmap words: B * ceil(T/32) * T * 4 bytes, rounded up to 256
+    assert lib.mla_attn_workspace_bytes(2, 4096, 2048) == 2 * 128 * 4096 * 4
+    assert lib.mla_attn_workspace_bytes(1, 100, 7) == (4 * 100 * 4 + 255) // 256 * 256
+    assert lib.mla_attn_workspace_bytes(0, 4096, 2048) == 0
+    assert lib.mla_attn_workspace_bytes(1, 40000, 2048) == 0
+    assert lib.mla_last_hip_error() == 0
+
+
+# Fake but aligned addresses: every call below must fail validation before touching them.
+A, B_, C, D, E, F, G = (0x100000 * i for i in range(1, 8))
+NOSTREAM = None
+
+
+def test_kv_latent_validation():
+    lib = _lib()
+    ok = dict(x=A, w=B_, g=C, eps=1e-6, cs=D, B=1, T=4, raw=E, ckv=F, kpe=G)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.mla_kv_latent(a["x"], a["w"], a["g"], a["eps"], a["cs"], a["B"], a["T"],
+                                 a["raw"], a["ckv"], a["kpe"], NOSTREAM)
+    assert call(x=None) == -1
+    assert call(kpe=None) == -1
+    assert call(B=0) == -2
+    assert call(T=-3) == -2
+    assert call(B=1 << 13, T=1 << 12) == -2            # B*T beyond MLA_MAX_ROWS
+    assert call(x=A + 2) == -3
+    assert call(ckv=F + 8) == -3
+    assert call(eps=0.0) == -7
+    assert call(eps=float("nan")) == -7
+    assert call(raw=A) == -8                            # output overlapping x
+    assert call(kpe=F) == -8                            # two outputs overlapping
+
+
+def test_norm_rope_validation():
+    lib = _lib()
+
+    def call(src=A, rows=4, stride=576, rope=1, g=C, eps=1e-6, cs=D, T=4, ckv=E, kpe=F):
+        return lib.mla_kv_norm_rope(src, rows, stride, rope, g, eps, cs, T, ckv, kpe, NOSTREAM)
+    assert call(src=None) == -1
+    assert call(cs=None) == -1
+    assert call(rows=0) == -2
+    assert call(stride=500) == -2
+    assert call(stride=512, rope=1) == -2               # rotary needs the 576-wide rows
+    assert call(T=0) == -2
+    assert call(g=C + 4) == -3
+    assert call(eps=-1.0) == -7
+    assert call(ckv=A + 16) == -8
+
+
+def test_kv_up_validation():
+    lib = _lib()
+    assert lib.mla_kv_up(None, B_, 1, 4, C, NOSTREAM) == -1
+    assert lib.mla_kv_up(A, B_, 0, 4, C, NOSTREAM) == -2
+    assert lib.mla_kv_up(A, B_ + 2, 1, 4, C, NOSTREAM) == -3
+    assert lib.mla_kv_up(A, B_, 1, 4, B_ + 1024, NOSTREAM) == -8
+
+
+def test_attention_and_bitmap_validation():
+    lib = _lib()
+    ws = lib.mla_attn_workspace_bytes(1, 64, 16)
+
+    def call(q=A, kv=B_, kpe=C, topk=D, B=1, T=64, K=16, scale=0.135, out=E, w=F, wsb=ws):
+        return lib.mla_sparse_prefill_attn(q, kv, kpe, topk, B, T, K, scale, out, w, wsb, NOSTREAM)
+    assert call(topk=None) == -1
+    assert call(w=None) == -1
+    assert call(K=0) == -2
+    assert call(T=40000) == -2
+    assert call(K=70000) == -2
+    assert call(out=E + 4) == -3
+    assert call(wsb=ws - 1) == -4
+    assert call(scale=0.0) == -7
+    assert call(scale=float("inf")) == -7
+    assert call(out=A + 64) == -8
+    assert call(w=E) == -8
+    assert lib.mla_selection_bitmap(None, 1, 64, 16, E, NOSTREAM) == -1
+    assert lib.mla_selection_bitmap(D, 1, 64, 16, None, NOSTREAM) == -1
+    assert lib.mla_selection_bitmap(D, 1, 0, 16, E, NOSTREAM) == -2
+    assert lib.mla_selection_bitmap(D + 4, 1, 64, 16, E, NOSTREAM) == -3
+    assert lib.mla_selection_bitmap(D, 1, 64, 16, D, NOSTREAM) == -8
+    assert lib.mla_rope_table(0, 10000.0, A, NOSTREAM) == -2
+    assert lib.mla_rope_table(8, 10000.0, None, NOSTREAM) == -1
+    assert lib.mla_rope_table(8, -1.0, A, NOSTREAM) == -7
