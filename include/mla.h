@@ -126,8 +126,9 @@ int mla_rope_table(int T, float theta, float* rope_cs, void* stream);
 int mla_kv_up(const void* c_kv, const void* w_ukv, int B, int T, void* kv, void* stream);
 
 /*
- * Bytes of workspace mla_sparse_prefill_attn needs (the selection bitmap, 4 * B * ceil(T/32) * T
- * bytes, rounded up to 256). Returns 0 for shapes the call would reject.
+ * Bytes of workspace mla_sparse_prefill_attn needs: the selection bitmap in the layout the
+ * attention kernel reads, 4 * B * (2 * ceil(T/64)) * (256 * ceil(T/256)) bytes (rounded up to
+ * 256). Returns 0 for shapes the call would reject.
  */
 size_t mla_attn_workspace_bytes(int B, int T, int K);
 

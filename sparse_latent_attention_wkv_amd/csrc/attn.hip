@@ -30,13 +30,15 @@ namespace mla {
 // ------------------------------------------------------------------------------------------------
 // Selection bitmap.
 // ------------------------------------------------------------------------------------------------
+// Output layout [B][Wout][Tout] with Wout >= ceil(T/32) words per query and Tout >= T query
+// columns; words and queries beyond the sequence are written as zero.
 template <int QR>
 __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* __restrict__ topk, int T, int K,
-                                                         int W, uint32_t* __restrict__ bitmap) {
-    extern __shared__ uint32_t rows_lds[];   // QR rows of W words (+1 pad word per row)
-    const int WP = W + 1;
+                                                         int Wout, int Tout, uint32_t* __restrict__ bitmap) {
+    extern __shared__ uint32_t rows_lds[];   // QR rows of Wout words (+1 pad word per row)
+    const int WP = Wout + 1;
     const int s0 = blockIdx.x * QR, b = blockIdx.y;
-    const int nrows = min(QR, T - s0);
+    const int nrows = max(0, min(QR, T - s0));
     for (int i = threadIdx.x; i < QR * WP; i += 256) rows_lds[i] = 0;
     __syncthreads();
 
@@ -66,46 +68,78 @@ __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* __restri
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < W * QR; i += 256) {
+    for (int i = threadIdx.x; i < Wout * QR; i += 256) {
         const int qi = i % QR, w = i / QR;
-        if (qi < nrows) bitmap[((size_t)b * W + w) * T + s0 + qi] = rows_lds[qi * WP + w];
+        if (s0 + qi < Tout) bitmap[((size_t)b * Wout + w) * Tout + s0 + qi] = rows_lds[qi * WP + w];
     }
 }
 
-hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap,
-                             hipStream_t stream) {
+hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout, int Tout,
+                             uint32_t* bitmap, hipStream_t stream) {
     constexpr int QR = 8;
-    const int W = (T + 31) / 32;
-    const dim3 grid((T + QR - 1) / QR, B);
-    const size_t lds = (size_t)QR * (W + 1) * sizeof(uint32_t);
-    sel_bitmap_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, W, bitmap);
+    const dim3 grid((Tout + QR - 1) / QR, B);
+    const size_t lds = (size_t)QR * (Wout + 1) * sizeof(uint32_t);
+    sel_bitmap_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, Wout, Tout, bitmap);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------------
 // Attention.
 // ------------------------------------------------------------------------------------------------
-constexpr int kKT = 64;                 // keys per LDS tile
-constexpr int kKsRow = kQkHead + 8;     // 200 bf16 = 400 B per staged key row
-constexpr int kVtRow = kKT + 8;         // 72 bf16 = 144 B per staged value feature row
+// Workgroup: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h). Key tiles of 64
+// are double-buffered in LDS; the next tile's global loads are in flight while the current tile
+// is computed, and one barrier per tile separates the stages.
+//
+// LDS stage (bytes), rows stored without padding and 16-byte chunks XOR-swizzled by row so the
+// MFMA operand reads are bank-conflict free:
+//   Kn  [64 keys][128] bf16, chunk ^= row & 15                   16384
+//   Kp  [64 keys][64]  bf16, chunk ^= row & 7                     8192
+//   V   [64 keys][128] bf16, chunk ^= 2 * (row & 3)              16384
+//   Bm  [2 words][256 queries] u32 (selection bits of the tile)   2048
+// V stays key-major; the transposing LDS read (ds_read_b64_tr_b16) delivers it as the
+// [feature][key] operand of O^T = V^T . P^T. Within each 16-lane group that read gives lane i,
+// slot k the element (i % 4) at the address of lane 4k + i/4, so a lane group addressing four
+// key rows x four feature quads receives 16 features x 4 keys transposed.
+constexpr int kKT = 64;
+constexpr int kWaves = 8;
+constexpr int kQT = kWaves * 32;
+constexpr int kOffKn = 0, kOffKp = 16384, kOffV = 24576, kOffBm = 40960, kStage = 43008;
 
-// Position of key k (0..63) of a tile inside a V^T row: within each group of 16 keys the four
-// quads are stored in the order 0, 2, 1, 3, so keys {4g..4g+3, 8+4g..8+4g+3} are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-    const int quad = (k >> 2) & 3;
-    const int pq = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-    return (k & ~15) + pq * 4 + (k & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_u8* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+__device__ __forceinline__ void lds_write16(lds_u8* p, const u32x4& v) {
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p) = v;
+}
+__device__ __forceinline__ uint32_t lds_read4(const lds_u8* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
+}
+__device__ __forceinline__ s16x4 lds_read_tr(const lds_u8* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int QB>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __restrict__ q,
+// max over the two lanes l and l ^ 32
+__device__ __forceinline__ float half_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const uint16_t* __restrict__ kpe,
                                                           const uint32_t* __restrict__ bitmap, int T,
-                                                          int nqt, float c2, uint16_t* __restrict__ out) {
-    constexpr int QT = 4 * 32 * QB;     // queries per workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kVHead * kVtRow];
+                                                          int Tpad, int Wp, int nqt, float c2,
+                                                          uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * kStage];
+    lds_u8* smem = (lds_u8*)smem_generic;
 
     // Workgroups are dealt to the 8 XCDs round-robin. Every query tile of one (b, h) goes to
     // the same XCD so the head's keys and values stay in that XCD's L2; within a head the
@@ -118,209 +152,213 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
-    const int W = (T + 31) >> 5;
-    const int q0 = qt * QT;
-    const int wq0 = q0 + wave * 32 * QB;
-    const int wq_last = min(T - 1, wq0 + 32 * QB - 1);
+    const int q0 = qt * kQT;
+    const int wq0 = q0 + wave * 32;
+    const int wq_last = min(T - 1, wq0 + 31);
+    const int qrow = wq0 + col;
 
     const uint16_t* kvh = kv + (size_t)bh * T * 256;
     const uint16_t* kpeb = kpe + (size_t)b * T * kRope;
-    const uint32_t* bmb = bitmap + (size_t)b * W * T;
+    const uint32_t* bmb = bitmap + (size_t)b * Wp * Tpad;
 
-    // Q^T fragments (B operand): lane holds query wq0 + 32*qb + col, features kc*16 + 8*half ...
-    bf16x8 qf[QB][12];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + qb * 32 + col;
+    // Q^T fragments (B operand of S^T = K . Q^T): lane holds query qrow, features kc*16 + 8*half.
+    bf16x8 qf[12];
+    {
         const uint16_t* src = q + (((size_t)b * T + qrow) * kHeads + h) * kQkHead + half * 8;
 #pragma unroll
         for (int kc = 0; kc < 12; ++kc)
-            qf[qb][kc] = as_bf16x8(qrow < T ? load16(src + kc * 16) : u32x4{0, 0, 0, 0});
+            qf[kc] = as_bf16x8(qrow < T ? load16(src + kc * 16) : u32x4{0, 0, 0, 0});
     }
 
-    f32x16 o[QB][4];
-    float m_run[QB], l_run[QB];
+    f32x16 o[4];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[qb][dt] = f32x16{};
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.f;
-    }
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
 
-    // Staging assignment. K: 64 keys x 24 chunks of 16 B (16 from the head's non-rotary key,
-    // 8 from the shared rotary key), six chunks per thread. V: thread owns 4 consecutive keys
-    // x 8 consecutive value features and writes them transposed.
-    const int v_dg = tid & 15, v_kg = tid >> 4;
-    const int v_dst = v_dg * 8 * kVtRow + vt_pos(v_kg * 4);
-    u32x4 kst[6], vst[4];
-
-    auto gload = [&](int t0) {
+    // ---- staging: 2 Kn + 1 Kp + 2 V chunks per thread, plus 1 bitmap chunk for threads < 128.
+    u32x4 r_kn[2], r_kp, r_v[2], r_bm;
+    auto gload = [&](int kt) {
+        const int t0 = kt * kKT;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int c = tid + 256 * i, key = c / 24, part = c - key * 24;
-            const int t = t0 + key;
-            u32x4 v = {0, 0, 0, 0};
-            if (t < T) v = part < 16 ? load16(kvh + (size_t)t * 256 + part * 8)
-                                     : load16(kpeb + (size_t)t * kRope + (part - 16) * 8);
-            kst[i] = v;
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 512 * i, row = c >> 4, lc = c & 15;
+            const int t = min(t0 + row, T - 1);
+            r_kn[i] = load16(kvh + (size_t)t * 256 + lc * 8);
+            r_v[i] = load16(kvh + (size_t)t * 256 + kNope + lc * 8);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = t0 + v_kg * 4 + k;
-            vst[k] = t < T ? load16(kvh + (size_t)t * 256 + kNope + v_dg * 8) : u32x4{0, 0, 0, 0};
+        {
+            const int row = tid >> 3, lc = tid & 7;
+            const int t = min(t0 + row, T - 1);
+            r_kp = load16(kpeb + (size_t)t * kRope + lc * 8);
+        }
+        if (tid < 128) {
+            const int ww = tid >> 6, q4 = (tid & 63) * 4;
+            r_bm = load16(bmb + (size_t)(kt * 2 + ww) * Tpad + q0 + q4);
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int stage) {
+        lds_u8* base = smem + stage * kStage;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int c = tid + 256 * i, key = c / 24, part = c - key * 24;
-            *reinterpret_cast<u32x4*>(&Ks[key * kKsRow + part * 8]) = kst[i];
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 512 * i, row = c >> 4, lc = c & 15;
+            lds_write16(base + kOffKn + row * 256 + ((lc ^ (row & 15)) << 4), r_kn[i]);
+            lds_write16(base + kOffV + row * 256 + ((lc ^ ((row & 3) << 1)) << 4), r_v[i]);
         }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-                u32x2 w;
-                w[0] = __builtin_amdgcn_perm(vst[1][jj], vst[0][jj], sel);
-                w[1] = __builtin_amdgcn_perm(vst[3][jj], vst[2][jj], sel);
-                *reinterpret_cast<u32x2*>(&Vt[v_dst + (2 * jj + e) * kVtRow]) = w;
-            }
+        {
+            const int row = tid >> 3, lc = tid & 7;
+            lds_write16(base + kOffKp + row * 128 + ((lc ^ (row & 7)) << 4), r_kp);
+        }
+        if (tid < 128) {
+            const int ww = tid >> 6, q4 = (tid & 63) * 4;
+            lds_write16(base + kOffBm + (ww * 256 + q4) * 4, r_bm);
         }
     };
 
-    const int q_last = min(T, q0 + QT) - 1;
+    // ---- per-lane LDS read offsets.
+    // K operand: key row (sub*32 + col), 16-byte chunk (2*kc + half) of the row, swizzled.
+    int kn_off[8], kp_off[4];
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) kn_off[kc] = kOffKn + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) kp_off[kc] = kOffKp + col * 128 + (((2 * kc + half) ^ (col & 7)) << 4);
+    // V operand via the transposing read: lane group g = lane/16, i = lane%16; the lane
+    // addresses key row (16c + 8n + 4*(g/2) + i/4) and feature quad 32dt + 16*(g%2) + 4*(i%4).
+    int v_off[4];
+    {
+        const int g = lane >> 4, i = lane & 15, k = i >> 2, qq = i & 3;
+        const int key = 4 * (g >> 1) + k;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int lc = 4 * dt + 2 * (g & 1) + (qq >> 1);
+            v_off[dt] = kOffV + key * 256 + ((lc ^ (k << 1)) << 4) + (qq & 1) * 8;
+        }
+    }
+    const int bm_off = kOffBm + (wave * 32 + col) * 4;
+
+    const int q_last = min(T, q0 + kQT) - 1;
     const int nkt = q_last / kKT + 1;
 
     gload(0);
-    lstore();
+    lstore(0);
+    if (nkt > 1) gload(1);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) gload((kt + 1) * kKT);
 
+    for (int kt = 0; kt < nkt; ++kt) {
+        const lds_u8* base = smem + (kt & 1) * kStage;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            const int kbase = kt * kKT + sub * 32;
-            if (kbase > wq_last) continue;          // every key is in this wave's future
+            const int kb = kt * kKT + sub * 32;
+            if (kb > wq_last) break;                      // keys all in this wave's future
+            const uint32_t word = lds_read4(base + bm_off + sub * 1024);
+            if (!__any(word != 0u)) continue;             // no query of this wave selects here
+            const bool full = __all(word == 0xFFFFFFFFu);
 
-            uint32_t word[QB];
-            bool any = false;
-            bool full[QB];
+            // S^T block: 32 keys x 32 queries, 192 features.
+            f32x16 s = f32x16{};
+            const lds_u8* kb_base = base + sub * 32 * 256;
+            const lds_u8* kp_base = base + sub * 32 * 128;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int qrow = wq0 + qb * 32 + col;
-                word[qb] = qrow < T ? bmb[(size_t)(kbase >> 5) * T + qrow] : 0u;
-                any |= __any(word[qb] != 0u);
-                full[qb] = __all(word[qb] == 0xFFFFFFFFu);
-            }
-            if (!any) continue;                     // no query of this wave selects a key here
+            for (int kc = 0; kc < 8; ++kc)
+                s = mfma32x32x16(as_bf16x8(lds_read16(kb_base + kn_off[kc])), qf[kc], s);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                s = mfma32x32x16(as_bf16x8(lds_read16(kp_base + kp_off[kc])), qf[8 + kc], s);
 
-            // S^T block: 32 keys x 32 queries per query block.
-            f32x16 s[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
-            const uint16_t* kfrag = &Ks[(sub * 32 + col) * kKsRow + half * 8];
-#pragma unroll
-            for (int kc = 0; kc < 12; ++kc) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kfrag + kc * 16));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qf[qb][kc], s[qb]);
-            }
-
-            bf16x8 pf[QB][2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if (!full[qb]) {
-                    // Accumulator r of this lane is key 8*(r/4) + 4*half + (r%4) of the block.
-                    const uint32_t w = word[qb] >> (4 * half);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int bit = 8 * (r >> 2) + (r & 3);
-                        s[qb][r] = ((w >> bit) & 1u) ? s[qb][r] : -INFINITY;
-                    }
-                }
-                float mx = s[qb][0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float m_new = fmaxf(m_run[qb], mx * c2);
-                const float base = m_new == -INFINITY ? 0.f : m_new;
-                float p[16];
-                float rs = 0.f;
+            if (!full) {
+                // accumulator r holds key 8*(r/4) + 4*half + (r%4) of the block
+                const uint32_t w = word >> (4 * half);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -base));
-                    rs += p[r];
-                }
-                rs += __shfl_xor(rs, 32, 64);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - base);
-                l_run[qb] = l_run[qb] * alpha + rs;
-                m_run[qb] = m_new;
-                if (__any(alpha != 1.f)) {
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[qb][dt][r] *= alpha;
-                }
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16(p[8 * c + 2 * i], p[8 * c + 2 * i + 1]);
-                    pf[qb][c] = as_bf16x8(pk);
+                    const int bit = 8 * (r >> 2) + (r & 3);
+                    const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe(w, bit, 1);
+                    s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xFF800000u & ~keep));
                 }
             }
+            float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+            mx = fmaxf(mx, s[15]);
+            const float mt = half_max(mx) * c2;
 
-            // O^T += V^T . P^T over the block's 32 keys (two 16-key reduction steps).
-            const uint16_t* vfrag = &Vt[col * kVtRow + sub * 32 + half * 8];
+            // Lazy rescale: the running max moves only when the block's max exceeds it by more
+            // than 2^8, so probabilities stay <= 256 and the O rescale is rare.
+            const bool need = mt > m_run + 8.0f;
+            if (__any(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+                if (need) m_run = mt;
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            }
+            const float nb = m_run == -INFINITY ? 0.f : -m_run;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, nb));
+            float rs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rs += p[r];
+            l_run += rs;
+            bf16x8 pf[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[i] = pack_bf16(p[8 * c + 2 * i], p[8 * c + 2 * i + 1]);
+                pf[c] = as_bf16x8(pk);
+            }
+
+            // O^T += V^T . P^T over the block's 32 keys, two 16-key steps.
+            const lds_u8* v_base = base + sub * 32 * 256;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 a =
-                        as_bf16x8(*reinterpret_cast<const u32x4*>(vfrag + dt * 32 * kVtRow + c * 16));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma32x32x16(a, pf[qb][c], o[qb][dt]);
+                    const s16x4 lo = lds_read_tr(v_base + v_off[dt] + (16 * c) * 256);
+                    const s16x4 hi = lds_read_tr(v_base + v_off[dt] + (16 * c + 8) * 256);
+                    typedef short s16x8 __attribute__((ext_vector_type(8)));
+                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf[c], o[dt]);
                 }
             }
         }
 
-        __syncthreads();
         if (kt + 1 < nkt) {
-            lstore();
-            __syncthreads();
+            lstore((kt + 1) & 1);
+            if (kt + 2 < nkt) gload(kt + 2);
         }
+        __syncthreads();
     }
 
-    // Epilogue: out[b, s, h, d] = O / l; lane owns features 8g + 4*half + 0..3 of each 32 block.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + qb * 32 + col;
-        if (qrow >= T) continue;
-        const float inv = 1.0f / l_run[qb];
+    // Epilogue: the two lane halves hold partial sums over different keys of the same query.
+    const float l_tot = half_sum(l_run);
+    if (qrow < T) {
+        const float inv = 1.0f / l_tot;
         uint16_t* dst = out + (((size_t)b * T + qrow) * kHeads + h) * kVHead;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 v;
-                v[0] = pack_bf16(o[qb][dt][4 * g] * inv, o[qb][dt][4 * g + 1] * inv);
-                v[1] = pack_bf16(o[qb][dt][4 * g + 2] * inv, o[qb][dt][4 * g + 3] * inv);
+                v[0] = pack_bf16(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+                v[1] = pack_bf16(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
                 store8(dst + dt * 32 + 8 * g + 4 * half, v);
             }
     }
 }
 
+int attn_bitmap_words(int T) { return 2 * ((T + kKT - 1) / kKT); }
+int attn_bitmap_cols(int T) { return (T + kQT - 1) / kQT * kQT; }
+
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint16_t* k_pe,
                               const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
                               hipStream_t stream) {
-    constexpr int QB = 1;
-    constexpr int QT = 4 * 32 * QB;
-    const int nqt = (T + QT - 1) / QT;
+    const int nqt = (T + kQT - 1) / kQT;
     const float c2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     const dim3 grid(B * kHeads * nqt);
-    sparse_attn_kernel<QB><<<grid, 256, 0, stream>>>(q, kv, k_pe, bitmap, T, nqt, c2, out);
+    sparse_attn_kernel<<<grid, 512, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
+                                                 attn_bitmap_words(T), nqt, c2, out);
     return hipGetLastError();
 }
 

@@ -102,7 +102,12 @@ int validate_topk(const int32_t* topk, int B, int T, int K) {
     return MLA_OK;
 }
 
-size_t bitmap_bytes(int B, int T) { return (size_t)B * ((T + 31) / 32) * T * sizeof(uint32_t); }
+// Bitmap as the attention kernel reads it (padded so every staged tile is in bounds).
+size_t attn_bitmap_bytes(int B, int T) {
+    return (size_t)B * mla::attn_bitmap_words(T) * mla::attn_bitmap_cols(T) * sizeof(uint32_t);
+}
+// Bitmap as mla_selection_bitmap returns it, [B][ceil(T/32)][T].
+size_t plain_bitmap_bytes(int B, int T) { return (size_t)B * ((T + 31) / 32) * T * sizeof(uint32_t); }
 
 }  // namespace
 
@@ -176,7 +181,7 @@ int mla_kv_up(const void* c_kv, const void* w_ukv, int B, int T, void* kv, void*
 
 size_t mla_attn_workspace_bytes(int B, int T, int K) {
     if (validate_topk(reinterpret_cast<const int32_t*>(16), B, T, K) != MLA_OK) return 0;
-    return (bitmap_bytes(B, T) + 255) & ~(size_t)255;
+    return (attn_bitmap_bytes(B, T) + 255) & ~(size_t)255;
 }
 
 int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap, void* stream) {
@@ -185,10 +190,11 @@ int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bit
     if (!bitmap) return MLA_E_NULL;
     if (!aligned16(bitmap)) return MLA_E_ALIGN;
     const Span ins[] = {{topk, (size_t)B * T * K * sizeof(int32_t)}};
-    const Span outs[] = {{bitmap, bitmap_bytes(B, T)}};
+    const Span outs[] = {{bitmap, plain_bitmap_bytes(B, T)}};
     if (any_alias(outs, 1, ins, 1)) return MLA_E_ALIAS;
     if ((st = check_device()) != MLA_OK) return st;
-    return launched(mla::launch_sel_bitmap(topk, B, T, K, bitmap, static_cast<hipStream_t>(stream)));
+    return launched(mla::launch_sel_bitmap(topk, B, T, K, (T + 31) / 32, T, bitmap,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
@@ -200,18 +206,19 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
     if (!aligned16(q) || !aligned16(kv) || !aligned16(k_pe) || !aligned16(out) || !aligned16(workspace))
         return MLA_E_ALIGN;
     if (!pos_finite(softmax_scale)) return MLA_E_ARG;
-    if (ws_bytes < bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
+    if (ws_bytes < attn_bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
     const size_t M = (size_t)B * T;
     const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
                         {kv, M * MLA_HEADS * 256 * kBf16},
                         {k_pe, M * MLA_ROPE * kBf16},
                         {topk, M * K * sizeof(int32_t)}};
-    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}, {workspace, bitmap_bytes(B, T)}};
+    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}, {workspace, attn_bitmap_bytes(B, T)}};
     if (any_alias(outs, 2, ins, 4)) return MLA_E_ALIAS;
     if ((st = check_device()) != MLA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t* bm = static_cast<uint32_t*>(workspace);
-    st = launched(mla::launch_sel_bitmap(topk, B, T, K, bm, s));
+    st = launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
+                                         mla::attn_bitmap_cols(T), bm, s));
     if (st != MLA_OK) return st;
     return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
                                             static_cast<const uint16_t*>(kv),

@@ -15,8 +15,12 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
                                hipStream_t stream);
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
                              hipStream_t stream);
-hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap,
-                             hipStream_t stream);
+// Selection bitmap [B][Wout][Tout] (Wout >= ceil(T/32), Tout >= T; the excess is zero-filled).
+hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout, int Tout,
+                             uint32_t* bitmap, hipStream_t stream);
+// Bitmap geometry the attention kernel reads: words per query column and query columns.
+int attn_bitmap_words(int T);
+int attn_bitmap_cols(int T);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint16_t* k_pe,
                               const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
                               hipStream_t stream);

@@ -47,9 +47,10 @@ def test_host_only_helpers():
     for code in range(-8, 0):
         assert lib.mla_status_string(code).startswith(b"MLA_E_")
     assert b"gfx950" in lib.mla_build_info()
-    # bitmap words: B * ceil(T/32) * T * 4 bytes, rounded up to 256
+    # bitmap words: B * (2 * ceil(T/64)) words x (256 * ceil(T/256)) query columns x 4 bytes
     assert lib.mla_attn_workspace_bytes(2, 4096, 2048) == 2 * 128 * 4096 * 4
-    assert lib.mla_attn_workspace_bytes(1, 100, 7) == (4 * 100 * 4 + 255) // 256 * 256
+    assert lib.mla_attn_workspace_bytes(1, 100, 7) == 4 * 256 * 4
+    assert lib.mla_attn_workspace_bytes(3, 16384, 2048) == 3 * 512 * 16384 * 4
     assert lib.mla_attn_workspace_bytes(0, 4096, 2048) == 0
     assert lib.mla_attn_workspace_bytes(1, 40000, 2048) == 0
     assert lib.mla_last_hip_error() == 0
