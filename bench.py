@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="headline", choices=["headline", "1k", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 256 MiB fill and copy so a counter "
+                         "run can scale FETCH_SIZE / WRITE_SIZE against known byte counts")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -168,6 +171,13 @@ def main():
     att = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.int32, device=dev)      # writes 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)                                                 # reads + writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     pairs = selected_pairs(d["topk"])
     attn_flop = 640.0 * pairs * 128

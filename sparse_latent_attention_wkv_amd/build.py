@@ -31,9 +31,17 @@ CFLAGS = [
 ]
 
 
+# Extra flags per source file.
+#  attn.hip: -fno-honor-nans lets fmaxf map to plain v_max (no NaN canonicalisation of MFMA
+#  results; the kernels never produce NaN from finite inputs).
+FILE_FLAGS = {
+    "attn.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

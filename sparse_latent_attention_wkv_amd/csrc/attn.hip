@@ -22,6 +22,8 @@
 // accumulator holds them (keys 4g..4g+3 and 8+4g..8+4g+3 for lane half g).
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
@@ -86,43 +88,55 @@ hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout,
 // ------------------------------------------------------------------------------------------------
 // Attention.
 // ------------------------------------------------------------------------------------------------
-// Workgroup: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h). Key tiles of 64
-// are double-buffered in LDS; the next tile's global loads are in flight while the current tile
-// is computed, and one barrier per tile separates the stages.
+// Workgroup: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h).
 //
-// LDS stage (bytes), rows stored without padding and 16-byte chunks XOR-swizzled by row so the
-// MFMA operand reads are bank-conflict free:
-//   Kn  [64 keys][128] bf16, chunk ^= row & 15                   16384
-//   Kp  [64 keys][64]  bf16, chunk ^= row & 7                     8192
-//   V   [64 keys][128] bf16, chunk ^= 2 * (row & 3)              16384
-//   Bm  [2 words][256 queries] u32 (selection bits of the tile)   2048
+// Key tiles of 64 keys (two 32-key blocks) rotate through three statically distinct LDS stages
+// filled by direct global->LDS loads; tile kt+2 is loaded while tile kt is computed, and one
+// barrier ends each tile.
+//
+// LDS stage, rows stored without padding, 16-byte chunks XOR-swizzled by row so that every
+// operand read is bank-conflict free (LDS serves 256 B per clock: 16 lanes of a 16-byte read,
+// 32 lanes of an 8-byte read):
+//   kn [64 keys][128] bf16 (256 B rows), chunk ^= row & 15
+//   kp [64 keys][64]  bf16 (128 B rows), chunk ^= (row >> 1) & 7
+//   v  [64 keys][128] bf16 (256 B rows), chunk ^= 4 * (row & 3)
+//   bm [2 words][256 queries] u32 (the tile's selection bits)
 // V stays key-major; the transposing LDS read (ds_read_b64_tr_b16) delivers it as the
 // [feature][key] operand of O^T = V^T . P^T. Within each 16-lane group that read gives lane i,
 // slot k the element (i % 4) at the address of lane 4k + i/4, so a lane group addressing four
 // key rows x four feature quads receives 16 features x 4 keys transposed.
+//
+// Software pipeline over 32-key blocks b of each wave:
+//   X_b:  S(b+1) MFMAs                    |  exponentials, packing and sums of block b
+//   (rare) rescale O for block b
+//   Y_b:  P.V MFMAs of block b            |  mask and row max of block b+1
+// so the matrix cores and the vector units of each wave have independent work, and the two
+// waves sharing a SIMD fill each other's stalls.
 constexpr int kKT = 64;
 constexpr int kWaves = 8;
-constexpr int kQT = kWaves * 32;
-constexpr int kOffKn = 0, kOffKp = 16384, kOffV = 24576, kOffBm = 40960, kStage = 43008;
+constexpr int kQW = 32;                  // queries per wave
+constexpr int kQT = kWaves * kQW;        // 256 queries per workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ u32x4 lds_read16(const lds_u8* p) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
-}
-__device__ __forceinline__ void lds_write16(lds_u8* p, const u32x4& v) {
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p) = v;
-}
-__device__ __forceinline__ uint32_t lds_read4(const lds_u8* p) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
-}
-__device__ __forceinline__ s16x4 lds_read_tr(const lds_u8* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(p));
-}
+struct Stage {
+    uint16_t* kn;
+    uint16_t* kp;
+    uint16_t* v;
+    uint32_t* bm;
+};
 
-// max over the two lanes l and l ^ 32
+__device__ __forceinline__ u32x4 lds_read16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// vmcnt(0): every global->LDS load of this wave has landed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x3F70); }
+
+// max / sum over the two lanes l and l ^ 32
 __device__ __forceinline__ float half_max(float v) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -132,14 +146,60 @@ __device__ __forceinline__ float half_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Softmax part 1 of a 32-key x 32-query S^T block held by this lane (16 keys of its query):
+// keys outside the selection become -inf, then the block's row max (over both lane halves).
+__device__ __forceinline__ float sm_mask_max(f32x16& s, uint32_t word, int half) {
+    // accumulator r holds key 8*(r/4) + 4*half + (r%4) of the block
+    const uint32_t w = word >> (4 * half);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int bit = 8 * (r >> 2) + (r & 3);
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe(w, bit, 1);
+        s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xFF800000u & ~keep));
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+    mx = fmaxf(mx, s[15]);
+    return half_max(mx);
+}
+
+// Softmax part 2: lazy running-max update (the max moves only when the block's max exceeds it
+// by more than 2^8 in base 2, so probabilities stay <= 256), rescale of the running sum,
+// probabilities packed as the bf16 B operand of the value MFMA, and their fp32 sum.
+__device__ __forceinline__ void sm_exp(const f32x16& s, float mx, float c2, float& m_run, float& l_run,
+                                       float& alpha, bf16x8 pf[2]) {
+    const float mt = mx * c2;
+    const bool need = mt > m_run + 8.0f;
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+    m_run = need ? mt : m_run;
+    l_run *= alpha;
+    const float nb = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u32x4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i], c2, nb));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i + 1], c2, nb));
+            pk[i] = pack_bf16(p0, p1);
+            l_run += p0 + p1;
+        }
+        pf[c] = as_bf16x8(pk);
+    }
+}
+
 __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const uint16_t* __restrict__ kpe,
                                                           const uint32_t* __restrict__ bitmap, int T,
                                                           int Tpad, int Wp, int nqt, float c2,
                                                           uint16_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * kStage];
-    lds_u8* smem = (lds_u8*)smem_generic;
+    __shared__ __attribute__((aligned(16))) uint16_t knA[kKT * 128], knB[kKT * 128], knC[kKT * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t kpA[kKT * 64], kpB[kKT * 64], kpC[kKT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t vA[kKT * 128], vB[kKT * 128], vC[kKT * 128];
+    __shared__ __attribute__((aligned(16))) uint32_t bmA[2 * kQT], bmB[2 * kQT], bmC[2 * kQT];
+    const Stage stA{knA, kpA, vA, bmA}, stB{knB, kpB, vB, bmB}, stC{knC, kpC, vC, bmC};
 
     // Workgroups are dealt to the 8 XCDs round-robin. Every query tile of one (b, h) goes to
     // the same XCD so the head's keys and values stay in that XCD's L2; within a head the
@@ -150,11 +210,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     const int qt = nqt - 1 - (j % nqt);
     const int b = bh / kHeads, h = bh - b * kHeads;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
     const int q0 = qt * kQT;
-    const int wq0 = q0 + wave * 32;
-    const int wq_last = min(T - 1, wq0 + 31);
+    const int wq0 = q0 + wave * kQW;
     const int qrow = wq0 + col;
 
     const uint16_t* kvh = kv + (size_t)bh * T * 256;
@@ -175,160 +235,134 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // ---- staging: 2 Kn + 1 Kp + 2 V chunks per thread, plus 1 bitmap chunk for threads < 128.
-    u32x4 r_kn[2], r_kp, r_v[2], r_bm;
-    auto gload = [&](int kt) {
+    // ---- global -> LDS loads of one tile. Each wave instruction moves 1 KB (64 lanes x 16 B) to
+    // consecutive LDS; the swizzle is applied by choosing which source chunk each lane fetches.
+    //   waves 0-3: kn rows 16w..16w+15 (4 instructions); waves 4-7: v rows 16(w-4).. (4);
+    //   every wave: kp rows 8w..8w+7 (1); waves 0-1: bm word w of the tile (1).
+    // Per-lane source offsets (elements from the tile's first row) are fixed; only the last
+    // tile, whose rows may run past the sequence, clamps rows to the last key (never selected).
+    const int r16 = lane >> 4;
+    int src_off[4];
+    const bool kn_wave = wave < 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = 16 * (wave & 3) + 4 * k + r16;
+        const int lc = kn_wave ? (lane & 15) ^ ((4 * k + r16) & 15) : (lane & 15) ^ (4 * r16);
+        src_off[k] = row * 256 + lc * 8 + (kn_wave ? 0 : kNope);
+    }
+    const int kp_row = 8 * wave + (lane >> 3);
+    const int kp_off = kp_row * kRope + ((lane & 7) ^ ((kp_row >> 1) & 7)) * 8;
+    auto issue_tile = [&](const Stage& st, int kt) {
         const int t0 = kt * kKT;
+        uint16_t* dst = kn_wave ? st.kn : st.v;
+        if (t0 + kKT <= T) {
+            const uint16_t* base = kvh + (size_t)t0 * 256;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i, row = c >> 4, lc = c & 15;
-            const int t = min(t0 + row, T - 1);
-            r_kn[i] = load16(kvh + (size_t)t * 256 + lc * 8);
-            r_v[i] = load16(kvh + (size_t)t * 256 + kNope + lc * 8);
-        }
-        {
-            const int row = tid >> 3, lc = tid & 7;
-            const int t = min(t0 + row, T - 1);
-            r_kp = load16(kpeb + (size_t)t * kRope + lc * 8);
-        }
-        if (tid < 128) {
-            const int ww = tid >> 6, q4 = (tid & 63) * 4;
-            r_bm = load16(bmb + (size_t)(kt * 2 + ww) * Tpad + q0 + q4);
-        }
-    };
-    auto lstore = [&](int stage) {
-        lds_u8* base = smem + stage * kStage;
+            for (int k = 0; k < 4; ++k) dma16(base + src_off[k], dst + (16 * (wave & 3) + 4 * k) * 128);
+            dma16(kpeb + (size_t)t0 * kRope + kp_off, st.kp + 8 * wave * 64);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i, row = c >> 4, lc = c & 15;
-            lds_write16(base + kOffKn + row * 256 + ((lc ^ (row & 15)) << 4), r_kn[i]);
-            lds_write16(base + kOffV + row * 256 + ((lc ^ ((row & 3) << 1)) << 4), r_v[i]);
+            for (int k = 0; k < 4; ++k) {
+                const int row = 16 * (wave & 3) + 4 * k + r16;
+                const int t = min(t0 + row, T - 1);
+                dma16(kvh + (size_t)t * 256 + (src_off[k] - row * 256), dst + (16 * (wave & 3) + 4 * k) * 128);
+            }
+            const int t = min(t0 + kp_row, T - 1);
+            dma16(kpeb + (size_t)t * kRope + (kp_off - kp_row * kRope), st.kp + 8 * wave * 64);
         }
-        {
-            const int row = tid >> 3, lc = tid & 7;
-            lds_write16(base + kOffKp + row * 128 + ((lc ^ (row & 7)) << 4), r_kp);
-        }
-        if (tid < 128) {
-            const int ww = tid >> 6, q4 = (tid & 63) * 4;
-            lds_write16(base + kOffBm + (ww * 256 + q4) * 4, r_bm);
-        }
+        if (wave < 2) dma16(bmb + (size_t)(kt * 2 + wave) * Tpad + q0 + lane * 4, st.bm + wave * kQT);
     };
 
-    // ---- per-lane LDS read offsets.
+    // ---- per-lane LDS read offsets (bytes).
     // K operand: key row (sub*32 + col), 16-byte chunk (2*kc + half) of the row, swizzled.
-    int kn_off[8], kp_off[4];
+    int kn_off[8], kpr_off[4], v_off[4];
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) kn_off[kc] = kOffKn + col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
+    for (int kc = 0; kc < 8; ++kc) kn_off[kc] = col * 256 + (((2 * kc + half) ^ (col & 15)) << 4);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) kp_off[kc] = kOffKp + col * 128 + (((2 * kc + half) ^ (col & 7)) << 4);
-    // V operand via the transposing read: lane group g = lane/16, i = lane%16; the lane
-    // addresses key row (16c + 8n + 4*(g/2) + i/4) and feature quad 32dt + 16*(g%2) + 4*(i%4).
-    int v_off[4];
+    for (int kc = 0; kc < 4; ++kc) kpr_off[kc] = col * 128 + (((2 * kc + half) ^ ((col >> 1) & 7)) << 4);
+    // V operand via the transposing read: lane group g = lane/16, i = lane%16; the lane addresses
+    // key row (16c + 8n + 4*(g/2) + i/4) and feature quad 32dt + 16*(g%2) + 4*(i%4).
     {
         const int g = lane >> 4, i = lane & 15, k = i >> 2, qq = i & 3;
         const int key = 4 * (g >> 1) + k;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             const int lc = 4 * dt + 2 * (g & 1) + (qq >> 1);
-            v_off[dt] = kOffV + key * 256 + ((lc ^ (k << 1)) << 4) + (qq & 1) * 8;
+            v_off[dt] = key * 256 + ((lc ^ (4 * k)) << 4) + (qq & 1) * 8;
         }
     }
-    const int bm_off = kOffBm + (wave * 32 + col) * 4;
+    const int bm_lane = wave * kQW + col;
+
+    auto s_block = [&](const Stage& st, int sub, f32x16& s) {
+        const uint8_t* kn = reinterpret_cast<const uint8_t*>(st.kn) + sub * 32 * 256;
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(st.kp) + sub * 32 * 128;
+        s = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) s = mfma32x32x16(as_bf16x8(lds_read16(kn + kn_off[kc])), qf[kc], s);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) s = mfma32x32x16(as_bf16x8(lds_read16(kp + kpr_off[kc])), qf[8 + kc], s);
+    };
+    auto pv_block = [&](const Stage& st, int sub, const bf16x8 pf[2]) {
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(st.v) + sub * 32 * 256;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const s16x4 lo = lds_read_tr(vb + v_off[dt] + (16 * c) * 256);
+                const s16x4 hi = lds_read_tr(vb + v_off[dt] + (16 * c + 8) * 256);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[dt] = mfma32x32x16(a, pf[c], o[dt]);
+            }
+        }
+    };
+
+    // Pipeline state carried between blocks: masked scores and row max of the next block.
+    f32x16 s_cur;
+    float mx_cur;
+
+    // One pipeline step: block b lives in (vs, vsub); block b+1 in (ks, ksub).
+    auto step = [&](const Stage& vs, int vsub, const Stage& ks, int ksub) {
+        f32x16 s_nx;
+        bf16x8 pf[2];
+        float alpha;
+        // X_b
+        s_block(ks, ksub, s_nx);
+        sm_exp(s_cur, mx_cur, c2, m_run, l_run, alpha, pf);
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        // Y_b
+        pv_block(vs, vsub, pf);
+        mx_cur = sm_mask_max(s_nx, ks.bm[ksub * kQT + bm_lane], half);
+        s_cur = s_nx;
+    };
+    // One tile kt in stage `cur`; `nxt` holds tile kt+1; `ld` receives tile kt+2.
+    auto tile = [&](int kt, int nkt, const Stage& cur, const Stage& nxt, const Stage& ld) {
+        if (kt + 2 < nkt) issue_tile(ld, kt + 2);
+        step(cur, 0, cur, 1);
+        step(cur, 1, nxt, 0);
+        wait_vm0();
+        __syncthreads();
+    };
 
     const int q_last = min(T, q0 + kQT) - 1;
     const int nkt = q_last / kKT + 1;
 
-    gload(0);
-    lstore(0);
-    if (nkt > 1) gload(1);
+    issue_tile(stA, 0);
+    if (nkt > 1) issue_tile(stB, 1);
+    wait_vm0();
     __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const lds_u8* base = smem + (kt & 1) * kStage;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int kb = kt * kKT + sub * 32;
-            if (kb > wq_last) break;                      // keys all in this wave's future
-            const uint32_t word = lds_read4(base + bm_off + sub * 1024);
-            if (!__any(word != 0u)) continue;             // no query of this wave selects here
-            const bool full = __all(word == 0xFFFFFFFFu);
-
-            // S^T block: 32 keys x 32 queries, 192 features.
-            f32x16 s = f32x16{};
-            const lds_u8* kb_base = base + sub * 32 * 256;
-            const lds_u8* kp_base = base + sub * 32 * 128;
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc)
-                s = mfma32x32x16(as_bf16x8(lds_read16(kb_base + kn_off[kc])), qf[kc], s);
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                s = mfma32x32x16(as_bf16x8(lds_read16(kp_base + kp_off[kc])), qf[8 + kc], s);
-
-            if (!full) {
-                // accumulator r holds key 8*(r/4) + 4*half + (r%4) of the block
-                const uint32_t w = word >> (4 * half);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int bit = 8 * (r >> 2) + (r & 3);
-                    const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe(w, bit, 1);
-                    s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xFF800000u & ~keep));
-                }
-            }
-            float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-            for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-            mx = fmaxf(mx, s[15]);
-            const float mt = half_max(mx) * c2;
-
-            // Lazy rescale: the running max moves only when the block's max exceeds it by more
-            // than 2^8, so probabilities stay <= 256 and the O rescale is rare.
-            const bool need = mt > m_run + 8.0f;
-            if (__any(need)) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-                if (need) m_run = mt;
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
-            const float nb = m_run == -INFINITY ? 0.f : -m_run;
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, nb));
-            float rs = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) rs += p[r];
-            l_run += rs;
-            bf16x8 pf[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 pk;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = pack_bf16(p[8 * c + 2 * i], p[8 * c + 2 * i + 1]);
-                pf[c] = as_bf16x8(pk);
-            }
-
-            // O^T += V^T . P^T over the block's 32 keys, two 16-key steps.
-            const lds_u8* v_base = base + sub * 32 * 256;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const s16x4 lo = lds_read_tr(v_base + v_off[dt] + (16 * c) * 256);
-                    const s16x4 hi = lds_read_tr(v_base + v_off[dt] + (16 * c + 8) * 256);
-                    typedef short s16x8 __attribute__((ext_vector_type(8)));
-                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf[c], o[dt]);
-                }
-            }
-        }
-
-        if (kt + 1 < nkt) {
-            lstore((kt + 1) & 1);
-            if (kt + 2 < nkt) gload(kt + 2);
-        }
-        __syncthreads();
+    s_block(stA, 0, s_cur);
+    mx_cur = sm_mask_max(s_cur, stA.bm[bm_lane], half);
+    for (int kt = 0; kt < nkt; kt += 3) {
+        tile(kt, nkt, stA, stB, stC);
+        if (kt + 1 >= nkt) break;
+        tile(kt + 1, nkt, stB, stC, stA);
+        if (kt + 2 >= nkt) break;
+        tile(kt + 2, nkt, stC, stA, stB);
     }
 
     // Epilogue: the two lane halves hold partial sums over different keys of the same query.
@@ -357,8 +391,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint1
     const int nqt = (T + kQT - 1) / kQT;
     const float c2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     const dim3 grid(B * kHeads * nqt);
-    sparse_attn_kernel<<<grid, 512, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
-                                                 attn_bitmap_words(T), nqt, c2, out);
+    sparse_attn_kernel<<<grid, kWaves * 64, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
+                                                         attn_bitmap_words(T), nqt, c2, out);
     return hipGetLastError();
 }
 
