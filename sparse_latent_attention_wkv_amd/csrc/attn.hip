@@ -106,12 +106,12 @@ hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout,
 // slot k the element (i % 4) at the address of lane 4k + i/4, so a lane group addressing four
 // key rows x four feature quads receives 16 features x 4 keys transposed.
 //
-// Software pipeline over 32-key blocks b of each wave:
-//   X_b:  S(b+1) MFMAs                    |  exponentials, packing and sums of block b
-//   (rare) rescale O for block b
-//   Y_b:  P.V MFMAs of block b            |  mask and row max of block b+1
-// so the matrix cores and the vector units of each wave have independent work, and the two
-// waves sharing a SIMD fill each other's stalls.
+// Software pipeline over 64-key tiles t of each wave:
+//   X_t:  S(t+1) MFMAs (two chains)       |  exponentials, packing and sums of tile t
+//   (rare) rescale O for tile t
+//   Y_t:  P.V MFMAs of tile t (8 chains)  |  mask and row max of tile t+1
+// so the matrix cores and the vector units of each wave have independent work, no wave runs a
+// single dependent MFMA chain, and the two waves sharing a SIMD fill each other's stalls.
 constexpr int kKT = 64;
 constexpr int kWaves = 8;
 constexpr int kQW = 32;                  // queries per wave
@@ -146,9 +146,10 @@ __device__ __forceinline__ float half_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Softmax part 1 of a 32-key x 32-query S^T block held by this lane (16 keys of its query):
-// keys outside the selection become -inf, then the block's row max (over both lane halves).
-__device__ __forceinline__ float sm_mask_max(f32x16& s, uint32_t word, int half) {
+// Softmax part 1 for one 64-key tile held by this lane as two 32-key x 32-query S^T blocks
+// (16 keys of its query each): keys outside the selection become -inf, then the tile's row max
+// over both lane halves.
+__device__ __forceinline__ void sm_mask(f32x16& s, uint32_t word, int half) {
     // accumulator r holds key 8*(r/4) + 4*half + (r%4) of the block
     const uint32_t w = word >> (4 * half);
 #pragma unroll
@@ -157,36 +158,45 @@ __device__ __forceinline__ float sm_mask_max(f32x16& s, uint32_t word, int half)
         const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe(w, bit, 1);
         s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xFF800000u & ~keep));
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+}
+__device__ __forceinline__ float sm_max(const f32x16 s[2]) {
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-    mx = fmaxf(mx, s[15]);
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[0][r]), s[0][r + 1]);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][r]), s[1][r + 1]);
+    mx = fmaxf(mx, s[0][15]);
     return half_max(mx);
 }
 
-// Softmax part 2: lazy running-max update (the max moves only when the block's max exceeds it
-// by more than 2^8 in base 2, so probabilities stay <= 256), rescale of the running sum,
-// probabilities packed as the bf16 B operand of the value MFMA, and their fp32 sum.
-__device__ __forceinline__ void sm_exp(const f32x16& s, float mx, float c2, float& m_run, float& l_run,
-                                       float& alpha, bf16x8 pf[2]) {
+// Softmax part 2 for one tile: lazy running-max update (the max moves only when the tile's max
+// exceeds it by more than 2^8 in base 2, so probabilities stay <= 256), rescale of the running
+// sum, probabilities packed as the bf16 B operands of the value MFMAs, and their fp32 sum.
+__device__ __forceinline__ void sm_exp(const f32x16 s[2], float mx, float c2, float& m_run, float& l_run,
+                                       float& alpha, bf16x8 pf[2][2]) {
     const float mt = mx * c2;
     const bool need = mt > m_run + 8.0f;
     alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
     m_run = need ? mt : m_run;
     l_run *= alpha;
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        u32x4 pk;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i], c2, nb));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i + 1], c2, nb));
-            pk[i] = pack_bf16(p0, p1);
-            l_run += p0 + p1;
+        for (int c = 0; c < 2; ++c) {
+            u32x4 pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[sb][8 * c + 2 * i], c2, nb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[sb][8 * c + 2 * i + 1], c2, nb));
+                pk[i] = pack_bf16(p0, p1);
+                acc0 += p0;
+                acc1 += p1;
+            }
+            pf[sb][c] = as_bf16x8(pk);
         }
-        pf[c] = as_bf16x8(pk);
-    }
+    l_run += acc0 + acc1;
 }
 
 __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
@@ -293,40 +303,57 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     }
     const int bm_lane = wave * kQW + col;
 
-    auto s_block = [&](const Stage& st, int sub, f32x16& s) {
-        const uint8_t* kn = reinterpret_cast<const uint8_t*>(st.kn) + sub * 32 * 256;
-        const uint8_t* kp = reinterpret_cast<const uint8_t*>(st.kp) + sub * 32 * 128;
-        s = f32x16{};
+    // S^T for both 32-key blocks of a tile: two independent MFMA chains sharing the Q operand.
+    auto s_tile = [&](const Stage& st, f32x16 s[2]) {
+        const uint8_t* kn = reinterpret_cast<const uint8_t*>(st.kn);
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(st.kp);
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) s = mfma32x32x16(as_bf16x8(lds_read16(kn + kn_off[kc])), qf[kc], s);
+        for (int kc = 0; kc < 8; ++kc) {
+            s[0] = mfma32x32x16(as_bf16x8(lds_read16(kn + kn_off[kc])), qf[kc], s[0]);
+            s[1] = mfma32x32x16(as_bf16x8(lds_read16(kn + 32 * 256 + kn_off[kc])), qf[kc], s[1]);
+        }
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) s = mfma32x32x16(as_bf16x8(lds_read16(kp + kpr_off[kc])), qf[8 + kc], s);
-    };
-    auto pv_block = [&](const Stage& st, int sub, const bf16x8 pf[2]) {
-        const uint8_t* vb = reinterpret_cast<const uint8_t*>(st.v) + sub * 32 * 256;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const s16x4 lo = lds_read_tr(vb + v_off[dt] + (16 * c) * 256);
-                const s16x4 hi = lds_read_tr(vb + v_off[dt] + (16 * c + 8) * 256);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[dt] = mfma32x32x16(a, pf[c], o[dt]);
-            }
+        for (int kc = 0; kc < 4; ++kc) {
+            s[0] = mfma32x32x16(as_bf16x8(lds_read16(kp + kpr_off[kc])), qf[8 + kc], s[0]);
+            s[1] = mfma32x32x16(as_bf16x8(lds_read16(kp + 32 * 128 + kpr_off[kc])), qf[8 + kc], s[1]);
         }
     };
+    auto pv_tile = [&](const Stage& st, const bf16x8 pf[2][2]) {
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(st.v);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const s16x4 lo = lds_read_tr(vb + v_off[dt] + (32 * sb + 16 * c) * 256);
+                    const s16x4 hi = lds_read_tr(vb + v_off[dt] + (32 * sb + 16 * c + 8) * 256);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[dt] = mfma32x32x16(a, pf[sb][c], o[dt]);
+                }
+            }
+    };
+    auto mask_tile = [&](const Stage& st, f32x16 s[2]) {
+        sm_mask(s[0], st.bm[bm_lane], half);
+        sm_mask(s[1], st.bm[kQT + bm_lane], half);
+        return sm_max(s);
+    };
 
-    // Pipeline state carried between blocks: masked scores and row max of the next block.
-    f32x16 s_cur;
+    // Pipeline state carried between tiles: masked scores and row max of the next tile.
+    f32x16 s_cur[2];
     float mx_cur;
 
-    // One pipeline step: block b lives in (vs, vsub); block b+1 in (ks, ksub).
-    auto step = [&](const Stage& vs, int vsub, const Stage& ks, int ksub) {
-        f32x16 s_nx;
-        bf16x8 pf[2];
+    // One tile t in stage `cur` (values) with tile t+1 in `nxt` (keys, selection bits) and tile
+    // t+2 loading into `ld`.
+    //   X_t: S(t+1) MFMAs | exponentials of t;  rare O rescale;  Y_t: P.V of t | mask, max of t+1
+    auto tile = [&](int kt, int nkt, const Stage& cur, const Stage& nxt, const Stage& ld) {
+        if (kt + 2 < nkt) issue_tile(ld, kt + 2);
+        f32x16 s_nx[2];
+        bf16x8 pf[2][2];
         float alpha;
-        // X_b
-        s_block(ks, ksub, s_nx);
+        s_tile(nxt, s_nx);
         sm_exp(s_cur, mx_cur, c2, m_run, l_run, alpha, pf);
         if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -334,16 +361,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // Y_b
-        pv_block(vs, vsub, pf);
-        mx_cur = sm_mask_max(s_nx, ks.bm[ksub * kQT + bm_lane], half);
-        s_cur = s_nx;
-    };
-    // One tile kt in stage `cur`; `nxt` holds tile kt+1; `ld` receives tile kt+2.
-    auto tile = [&](int kt, int nkt, const Stage& cur, const Stage& nxt, const Stage& ld) {
-        if (kt + 2 < nkt) issue_tile(ld, kt + 2);
-        step(cur, 0, cur, 1);
-        step(cur, 1, nxt, 0);
+        pv_tile(cur, pf);
+        mx_cur = mask_tile(nxt, s_nx);
+        s_cur[0] = s_nx[0];
+        s_cur[1] = s_nx[1];
         wait_vm0();
         __syncthreads();
     };
@@ -355,8 +376,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     if (nkt > 1) issue_tile(stB, 1);
     wait_vm0();
     __syncthreads();
-    s_block(stA, 0, s_cur);
-    mx_cur = sm_mask_max(s_cur, stA.bm[bm_lane], half);
+    s_tile(stA, s_cur);
+    mx_cur = mask_tile(stA, s_cur);
     for (int kt = 0; kt < nkt; kt += 3) {
         tile(kt, nkt, stA, stB, stC);
         if (kt + 1 >= nkt) break;
