@@ -103,7 +103,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=["headline", "1k", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 256 MiB fill and copy so a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE against known byte counts")
