@@ -166,14 +166,167 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
     return hipGetLastError();
 }
 
+
+
+// ------------------------------------------------------------------------------------------------
+// Up-projection GEMM, second form: 128 tokens x 256 features (one head) per 4-wave workgroup,
+// each wave 64 x 128. K streams in chunks of 32 through a three-stage LDS ring (72 KB, so two
+// workgroups share a CU) filled by direct global->LDS loads issued two chunks ahead: no staging
+// registers, and one workgroup's barriers and prologue overlap the other's MFMAs. LDS rows are
+// 64 bytes (32 bf16); 16-byte chunk c of row r is stored at c ^ ((r >> 2) & 3), which keeps the
+// 16-lane operand reads conflict free. The epilogue stages the bf16 tile through LDS so every
+// global store writes whole 512-byte head rows (16 bytes per lane).
+// ------------------------------------------------------------------------------------------------
+namespace up2 {
+constexpr int BM = 128, BN = 256, BK = 32, STAGES = 3;
+constexpr int ROWB = BK * 2;                                 // 64 bytes per LDS row
+constexpr int XB = BM * ROWB, WB = BN * ROWB;                // 8 KB and 16 KB per stage
+}
+
+__device__ __forceinline__ void dma16_g(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Workgroup barrier without the release fence of __syncthreads(), whose wait would drain every
+// outstanding global->LDS load and so the prefetch ring. This thread's LDS reads are completed
+// first, so no later load into a stage can overtake a read of it; the global->LDS loads that
+// must have landed are waited for explicitly with vmcnt before the barrier.
+__device__ __forceinline__ void barrier_keep_loads() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict__ X,
+                                                      const uint16_t* __restrict__ W, int M, int T,
+                                                      int mtiles, uint16_t* __restrict__ out) {
+    using namespace up2;
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[XB], xs1[XB], xs2[XB];
+    __shared__ __attribute__((aligned(16))) uint8_t ws0[WB], ws1[WB], ws2[WB];
+    uint8_t* const xs[STAGES] = {xs0, xs1, xs2};
+    uint8_t* const ws[STAGES] = {ws0, ws1, ws2};
+
+    // Consecutive workgroups sweep the token tiles of one head; XCD x (workgroups are dealt
+    // round-robin) then holds token tiles x, x+8, ... for every head in its L2.
+    const int h = blockIdx.x / mtiles, mt = blockIdx.x % mtiles;
+    const int m0 = mt * BM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // DMA: a stage is 8 one-KB loads of X rows and 16 of W rows; wave w loads X rows 32w..32w+31
+    // and W rows 64w..64w+63, six loads in all, so every wave has the same count in flight. A
+    // 1 KB load covers 16 rows of 64 bytes; lane i writes row (i >> 2), physical chunk (i & 3),
+    // so it fetches logical chunk (i & 3) ^ ((row >> 2) & 3).
+    int x_src[2], w_src[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int xr = 32 * wave + 16 * j + (lane >> 2);
+        x_src[j] = (min(m0 + xr, M - 1) - m0) * kLora + (((lane & 3) ^ ((xr >> 2) & 3)) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int wr = 64 * wave + 16 * j + (lane >> 2);
+        w_src[j] = wr * kLora + (((lane & 3) ^ ((wr >> 2) & 3)) * 8);
+    }
+    const uint16_t* xbase = X + (size_t)m0 * kLora;
+    const uint16_t* wbase = W + (size_t)h * BN * kLora;
+    auto issue = [&](int kc, uint8_t* xdst, uint8_t* wdst) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16_g(xbase + kc * BK + x_src[j], xdst + (32 * wave + 16 * j) * ROWB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16_g(wbase + kc * BK + w_src[j], wdst + (64 * wave + 16 * j) * ROWB);
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+    // MFMA operand reads: row (l % 32) of a 32-row block, 16-byte chunk (2s + l/32), swizzled.
+    const int fr = lane & 31, fh = lane >> 5;
+    int x_off[2][2], w_off[4][2];   // [block][k-step of 16]
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int row = wm * 64 + b * 32 + fr;
+            x_off[b][s] = row * ROWB + (((2 * s + fh) ^ ((row >> 2) & 3)) << 4);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int row = wn * 128 + a * 32 + fr;
+            w_off[a][s] = row * ROWB + (((2 * s + fh) ^ ((row >> 2) & 3)) << 4);
+        }
+    }
+
+    constexpr int NK = kLora / BK;   // 16 chunks
+    issue(0, xs[0], ws[0]);
+    issue(1, xs[1], ws[1]);
+    __builtin_amdgcn_s_waitcnt(0x3F76);          // vmcnt(6): chunk 0 landed
+    barrier_keep_loads();
+#pragma unroll
+    for (int kc = 0; kc < NK; ++kc) {
+        const int st = kc % 3;
+        if (kc + 2 < NK) issue(kc + 2, xs[(kc + 2) % 3], ws[(kc + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);       // keep the loads at the top of the chunk
+        const uint8_t* xb = xs[st];
+        const uint8_t* wb = ws[st];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 bx[2], aw[4];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(xb + x_off[b][s]));
+#pragma unroll
+            for (int a = 0; a < 4; ++a) aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(wb + w_off[a][s]));
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
+        }
+        // chunk kc+1 must have landed; chunk kc+2's loads may stay in flight
+        if (kc + 2 < NK)
+            __builtin_amdgcn_s_waitcnt(0x3F76);      // vmcnt(6)
+        else
+            __builtin_amdgcn_s_waitcnt(0x3F70);      // vmcnt(0)
+        barrier_keep_loads();
+    }
+
+    // Epilogue: each wave stages one 32-token x 128-feature block at a time in its own 8 KB of
+    // the (now idle) W ring, rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
+    // writes it back as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store).
+    // The barrier ending the K loop (after vmcnt(0)) guarantees that no wave still reads the
+    // ring and no load into it is in flight.
+    uint8_t* ot = (wave < 2 ? ws0 : ws1) + (wave & 1) * 8192;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 v;
+                v[0] = pack_bf16(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
+                v[1] = pack_bf16(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
+                const int chunk = (4 * a + g) ^ (fr & 15);
+                *reinterpret_cast<u32x2*>(ot + fr * 256 + chunk * 16 + fh * 8) = v;
+            }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4), c = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+            const int m = m0 + wm * 64 + b * 32 + row;
+            if (m < M) {
+                const int bb = m / T, t = m - bb * T;
+                store16(out + (((size_t)bb * kHeads + h) * T + t) * 256 + wn * 128 + c * 8, v);
+            }
+        }
+    }
+}
+
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
                              hipStream_t stream) {
-    constexpr int BM = 128, BN = 256;
     const int M = B * T;
-    const int mtiles = (M + BM - 1) / BM, ntiles = kHeads;
-    const dim3 grid(mtiles * ntiles);
-    gemm_nt_kernel<BM, BN, 2, 2, kModeUp><<<grid, 256, 0, stream>>>(c_kv, w_ukv, M, kLora, T, mtiles,
-                                                                    ntiles, kv);
+    const int mtiles = (M + up2::BM - 1) / up2::BM;
+    gemm_up_kernel<<<mtiles * kHeads, 256, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
     return hipGetLastError();
 }
 
