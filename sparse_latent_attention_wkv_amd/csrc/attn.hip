@@ -130,8 +130,17 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *reinterpret
 __device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+__device__ __forceinline__ uint32_t uniform32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t x = (uint64_t)(size_t)p;
+    return (const void*)(size_t)(((uint64_t)uniform32((uint32_t)(x >> 32)) << 32) | uniform32((uint32_t)x));
+}
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, void* lds) {
+    const uint32_t l = uniform32((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(l)
+                 : "memory", "m0");
 }
 // vmcnt(0): every global->LDS load of this wave has landed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x3F70); }
@@ -252,35 +261,29 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     // Per-lane source offsets (elements from the tile's first row) are fixed; only the last
     // tile, whose rows may run past the sequence, clamps rows to the last key (never selected).
     const int r16 = lane >> 4;
-    int src_off[4];
+    uint32_t src_off[4];   // bytes from the tile's first row
     const bool kn_wave = wave < 4;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int row = 16 * (wave & 3) + 4 * k + r16;
         const int lc = kn_wave ? (lane & 15) ^ ((4 * k + r16) & 15) : (lane & 15) ^ (4 * r16);
-        src_off[k] = row * 256 + lc * 8 + (kn_wave ? 0 : kNope);
+        src_off[k] = (uint32_t)(row * 512 + lc * 16 + (kn_wave ? 0 : 2 * kNope));
     }
     const int kp_row = 8 * wave + (lane >> 3);
-    const int kp_off = kp_row * kRope + ((lane & 7) ^ ((kp_row >> 1) & 7)) * 8;
+    const uint32_t kp_off = (uint32_t)(kp_row * 2 * kRope + (((lane & 7) ^ ((kp_row >> 1) & 7)) << 4));
     auto issue_tile = [&](const Stage& st, int kt) {
         const int t0 = kt * kKT;
         uint16_t* dst = kn_wave ? st.kn : st.v;
-        if (t0 + kKT <= T) {
-            const uint16_t* base = kvh + (size_t)t0 * 256;
+        const int tl = T - 1 - t0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dma16(base + src_off[k], dst + (16 * (wave & 3) + 4 * k) * 128);
-            dma16(kpeb + (size_t)t0 * kRope + kp_off, st.kp + 8 * wave * 64);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int row = 16 * (wave & 3) + 4 * k + r16;
-                const int t = min(t0 + row, T - 1);
-                dma16(kvh + (size_t)t * 256 + (src_off[k] - row * 256), dst + (16 * (wave & 3) + 4 * k) * 128);
-            }
-            const int t = min(t0 + kp_row, T - 1);
-            dma16(kpeb + (size_t)t * kRope + (kp_off - kp_row * kRope), st.kp + 8 * wave * 64);
+        for (int k = 0; k < 4; ++k) {
+            const int row = 16 * (wave & 3) + 4 * k + r16;
+            const int dr = min(row, tl) - row;
+            dma16s(kvh + (size_t)t0 * 256, src_off[k] + (uint32_t)(dr * 512), dst + (16 * (wave & 3) + 4 * k) * 128);
         }
-        if (wave < 2) dma16(bmb + (size_t)(kt * 2 + wave) * Tpad + q0 + lane * 4, st.bm + wave * kQT);
+        const int drp = min(kp_row, tl) - kp_row;
+        dma16s(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp + 8 * wave * 64);
+        if (wave < 2) dma16s(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm + wave * kQT);
     };
 
     // ---- per-lane LDS read offsets (bytes).
