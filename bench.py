@@ -96,6 +96,61 @@ def cpu_baseline(d: dict, B: int, T: int, heads_sample: int) -> dict:
             "sample_seconds": round(t3 - t0, 2)}
 
 
+def timed_us(torch, stream, fn, reps: int = 20, warm: int = 5) -> float:
+    """Mean GPU time of fn() in microseconds: events around `reps` back-to-back calls."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def side_measurements(torch, mla, dev, stream, topk, B: int, T: int, K: int) -> dict:
+    """Bandwidth-bound kernels against the HBM roofline, outside the timed step: the latent
+    norm/rotary at the front-end shape (8 x 4096 rows of 576; 2304 B per row) and the selection
+    bitmap at the benchmarked shape (reads B*T*K*4 B, writes B*ceil(T/32)*T*4 B)."""
+    torch.manual_seed(1005)
+    rows, t_rope = 8 * 4096, 4096
+    kv_raw = torch.randn((rows, 576), device=dev).to(torch.bfloat16)
+    gain = 1.0 + 0.1 * torch.randn(512, device=dev)
+    rope_cs = mla.mla_rope_table(t_rope, dev)
+    c_kv = torch.empty((rows, 512), dtype=torch.bfloat16, device=dev)
+    k_pe = torch.empty((rows, 64), dtype=torch.bfloat16, device=dev)
+    us = timed_us(torch, stream, lambda: mla.mla_kv_norm_rope(kv_raw, gain, 1e-6, rope_cs, t_rope, out=(c_kv, k_pe)))
+    nbytes = 2304.0 * rows
+    norm = {"rows": rows, "us": us, "GB_s": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes}
+    bm = torch.empty((B, (T + 31) // 32, T), dtype=torch.int32, device=dev)
+    us_bm = timed_us(torch, stream, lambda: mla.mla_selection_bitmap(topk, out=bm))
+    bm_bytes = 4.0 * B * T * K + 4.0 * B * ((T + 31) // 32) * T
+    bitmap = {"us": us_bm, "GB_s": bm_bytes / (us_bm * 1e-6) / 1e9,
+              "frac_hbm": bm_bytes / (us_bm * 1e-6) / 1e9 / PEAK_HBM_GBS, "bytes": bm_bytes}
+    del kv_raw, c_kv, k_pe, bm
+    return {"norm_rope_frontend_B8_T4096": norm, "selection_bitmap": bitmap}
+
+
+def mfma_busy_record():
+    """MFMA-busy fraction of the attention kernel from a rocprofv3 counter run, if the record
+    matches the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "sparse_attn_traffic.txt")
+    src = os.path.join(ROOT, "sparse_latent_attention_wkv_amd", "csrc", "attn.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("source_sha") != sha or "mfma_busy_frac" not in kv:
+        return None
+    return float(kv["mfma_busy_frac"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +227,8 @@ def main():
     gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
 
+    side = side_measurements(torch, mla, dev, stream, topk, B, T, K)
+
     if args.copy_calibration:
         src = torch.ones(1 << 26, dtype=torch.int32, device=dev)      # writes 256 MiB
         dst = torch.empty_like(src)
@@ -212,6 +269,9 @@ def main():
         "stages_ms": {"kv_latent": lat, "kv_up": upm, "sparse_attn": att, "gpu_step": gpu_step},
         "stage_tflops": {"kv_latent": flop_down / (lat * 1e-3) / 1e12,
                          "kv_up": flop_up / (upm * 1e-3) / 1e12},
+        "attention_only_tokens_per_s": tokens / (att * 1e-3),
+        "attention_mfma_busy_frac": mfma_busy_record(),
+        "bandwidth_kernels": side,
         "selected_pairs_all_batches": pairs,
         "scored_over_selected_upper_bound": causal_pairs / pairs,
         "input_generation_s": round(t_gen, 2),

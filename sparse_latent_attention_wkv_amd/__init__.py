@@ -125,21 +125,30 @@ def mla_kv_latent(x, w_dkv, kv_gain, eps: float = 1e-6, rope_cs=None, out=None):
     return kv_raw, c_kv, k_pe
 
 
-def mla_kv_norm_rope(kv_raw, gain, eps: float = 1e-6, rope_cs=None, T: int | None = None):
+def mla_kv_norm_rope(kv_raw, gain, eps: float = 1e-6, rope_cs=None, T: int | None = None, out=None):
     """kv_raw [rows, 576] (latent + rotary key) or [rows, 512] (latent only) bf16 ->
-    (c_kv [rows, 512], k_pe [rows, 64] or None). Row r is at position r % T for the rotary."""
+    (c_kv [rows, 512], k_pe [rows, 64] or None). Row r is at position r % T for the rotary.
+    `out` = (c_kv, k_pe) reuses caller buffers."""
     if kv_raw.dim() != 2:
         raise ValueError("kv_raw must be 2-D [rows, 576 or 512]")
     rows, stride = kv_raw.shape
     _need(kv_raw, "kv_raw", torch.bfloat16)
     _need(gain, "gain", torch.float32, (KV_LORA,))
     has_rope = rope_cs is not None
-    c_kv = torch.empty((rows, KV_LORA), dtype=torch.bfloat16, device=kv_raw.device)
-    k_pe = None
+    if out is not None:
+        c_kv, k_pe = out
+        _need(c_kv, "c_kv", torch.bfloat16, (rows, KV_LORA))
+    else:
+        c_kv = torch.empty((rows, KV_LORA), dtype=torch.bfloat16, device=kv_raw.device)
+        k_pe = None
     if has_rope:
         T = rope_cs.shape[0] if T is None else T
         _need(rope_cs, "rope_cs", torch.float32, (T, 32, 2))
-        k_pe = torch.empty((rows, ROPE), dtype=torch.bfloat16, device=kv_raw.device)
+        if k_pe is None:
+            k_pe = torch.empty((rows, ROPE), dtype=torch.bfloat16, device=kv_raw.device)
+        _need(k_pe, "k_pe", torch.bfloat16, (rows, ROPE))
+    else:
+        k_pe = None
     with torch.cuda.device(kv_raw.device):
         _check(lib().mla_kv_norm_rope(_ptr(kv_raw), rows, stride, int(has_rope), _ptr(gain), eps,
                                       _ptr(rope_cs), T or 1, _ptr(c_kv), _ptr(k_pe),
@@ -162,13 +171,18 @@ def mla_kv_up(c_kv, w_ukv, out=None):
     return out
 
 
-def mla_selection_bitmap(topk):
-    """topk [B, T, K] int32 -> bitmap [B, ceil(T/32), T] int32 (bit t%32 of word t/32 of row s)."""
+def mla_selection_bitmap(topk, out=None):
+    """topk [B, T, K] int32 -> bitmap [B, ceil(T/32), T] int32 (bit t%32 of word t/32 of row s).
+    `out` reuses a caller buffer of that shape."""
     if topk.dim() != 3:
         raise ValueError("topk must be [B, T, K]")
     B, T, K = topk.shape
     _need(topk, "topk", torch.int32)
-    bm = torch.empty((B, (T + 31) // 32, T), dtype=torch.int32, device=topk.device)
+    if out is not None:
+        bm = out
+        _need(bm, "bitmap", torch.int32, (B, (T + 31) // 32, T))
+    else:
+        bm = torch.empty((B, (T + 31) // 32, T), dtype=torch.int32, device=topk.device)
     with torch.cuda.device(topk.device):
         _check(lib().mla_selection_bitmap(_ptr(topk), B, T, K, _ptr(bm), _stream(topk.device)))
     return bm
