@@ -6,9 +6,10 @@
 // projection output splits into the 512 latent and the 64-wide rotary key; the key is rotated
 // by the position's freqs_cis entry, adjacent pairs read as complex numbers.
 //
-// Layout: one wave per row. Lane l reads latent features 8l..8l+7 with one 16-byte load; lanes
-// 0..31 also rotate pair l of the rotary key (one 4-byte load, one 8-byte table load). The mean
-// of squares is a 64-lane butterfly sum.
+// Layout: one wave per row, four rows per wave with all their loads issued before any arithmetic
+// (enough bytes in flight per wave to stream at HBM rate). Lane l reads latent features
+// 8l..8l+7 with one 16-byte load; lanes 0..31 also rotate pair l of the rotary key (one 4-byte
+// load, one 8-byte table load). The mean of squares is a 64-lane butterfly sum.
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const uint16_t* __restri
 hipError_t launch_norm_rope(const uint16_t* src, int rows, int stride, bool rope, const float* gain,
                             float eps, const float* rope_cs, int T, uint16_t* c_kv, uint16_t* k_pe,
                             hipStream_t stream) {
-    constexpr int R = 2;
+    constexpr int R = 4;
     const int per_block = 4 * R;
     const dim3 grid((rows + per_block - 1) / per_block);
     if (rope)
