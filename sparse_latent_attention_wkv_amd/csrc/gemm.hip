@@ -169,18 +169,25 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
 
 
 // ------------------------------------------------------------------------------------------------
-// Up-projection GEMM, second form: 128 tokens x 256 features (one head) per 4-wave workgroup,
-// each wave 64 x 128. K streams in chunks of 32 through a three-stage LDS ring (72 KB, so two
-// workgroups share a CU) filled by direct global->LDS loads issued two chunks ahead: no staging
-// registers, and one workgroup's barriers and prologue overlap the other's MFMAs. LDS rows are
-// 64 bytes (32 bf16); 16-byte chunk c of row r is stored at c ^ ((r >> 2) & 3), which keeps the
-// 16-lane operand reads conflict free. The epilogue stages the bf16 tile through LDS so every
-// global store writes whole 512-byte head rows (16 bytes per lane).
+// Up-projection GEMM, second form: BM tokens x 256 features (one head) per workgroup of BM/32
+// waves (BM/64 along tokens x 2 along features), each wave 64 x 128. K streams in chunks of 32
+// through a three-stage LDS ring filled by direct global->LDS loads issued two chunks ahead: no
+// staging registers. LDS rows are 64 bytes (32 bf16); 16-byte chunk c of row r is stored at
+// c ^ ((r >> 2) & 3), which keeps the 16-lane operand reads conflict free. The epilogue stages
+// each wave's bf16 blocks in LDS so every global store writes whole 256-byte half rows.
+// BM = 128 (four waves, 72 KB: two workgroups share a CU) or 256 (eight waves, 96 KB: operands
+// reused over twice the tokens).
 // ------------------------------------------------------------------------------------------------
+#ifndef UP_BM
+#define UP_BM 256
+#endif
 namespace up2 {
-constexpr int BM = 128, BN = 256, BK = 32, STAGES = 3;
+#ifndef UP_STAGES
+#define UP_STAGES 3
+#endif
+constexpr int BN = 256, BK = 32, STAGES = UP_STAGES;
 constexpr int ROWB = BK * 2;                                 // 64 bytes per LDS row
-constexpr int XB = BM * ROWB, WB = BN * ROWB;                // 8 KB and 16 KB per stage
+constexpr int WB = BN * ROWB;                                // 16 KB of W rows per stage
 }
 
 __device__ __forceinline__ void dma16_g(const void* g, void* lds) {
@@ -195,14 +202,19 @@ __device__ __forceinline__ void barrier_keep_loads() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict__ X,
-                                                      const uint16_t* __restrict__ W, int M, int T,
-                                                      int mtiles, uint16_t* __restrict__ out) {
+template <int BM>
+__global__ __launch_bounds__(BM * 2) void gemm_up_kernel(const uint16_t* __restrict__ X,
+                                                         const uint16_t* __restrict__ W, int M, int T,
+                                                         int mtiles, uint16_t* __restrict__ out) {
     using namespace up2;
-    __shared__ __attribute__((aligned(16))) uint8_t xs0[XB], xs1[XB], xs2[XB];
-    __shared__ __attribute__((aligned(16))) uint8_t ws0[WB], ws1[WB], ws2[WB];
-    uint8_t* const xs[STAGES] = {xs0, xs1, xs2};
-    uint8_t* const ws[STAGES] = {ws0, ws1, ws2};
+    constexpr int NW = BM / 32;                  // waves
+    constexpr int XB = BM * ROWB;                // X rows per stage
+    constexpr int WLOADS = 16 / NW;              // 1 KB W loads per wave per chunk
+    constexpr int LOADS = 2 + WLOADS;            // loads per wave per chunk (2 of X)
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[XB], xs1[XB], xs2[XB], xs3[STAGES > 3 ? XB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ws0[WB], ws1[WB], ws2[WB], ws3[STAGES > 3 ? WB : 16];
+    uint8_t* const xs[4] = {xs0, xs1, xs2, xs3};
+    uint8_t* const ws[4] = {ws0, ws1, ws2, ws3};
 
     // Consecutive workgroups sweep the token tiles of one head; XCD x (workgroups are dealt
     // round-robin) then holds token tiles x, x+8, ... for every head in its L2.
@@ -210,21 +222,21 @@ __global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict
     const int m0 = mt * BM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % (BM / 64), wn = wave / (BM / 64);
 
-    // DMA: a stage is 8 one-KB loads of X rows and 16 of W rows; wave w loads X rows 32w..32w+31
-    // and W rows 64w..64w+63, six loads in all, so every wave has the same count in flight. A
-    // 1 KB load covers 16 rows of 64 bytes; lane i writes row (i >> 2), physical chunk (i & 3),
-    // so it fetches logical chunk (i & 3) ^ ((row >> 2) & 3).
-    int x_src[2], w_src[4];
+    // DMA: a stage is BM/16 one-KB loads of X rows and 16 of W rows; wave w loads X rows
+    // 32w..32w+31 and W rows (16 WLOADS) w.., so every wave has the same count in flight. A 1 KB
+    // load covers 16 rows of 64 bytes; lane i writes row (i >> 2), physical chunk (i & 3), so it
+    // fetches logical chunk (i & 3) ^ ((row >> 2) & 3).
+    int x_src[2], w_src[WLOADS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int xr = 32 * wave + 16 * j + (lane >> 2);
         x_src[j] = (min(m0 + xr, M - 1) - m0) * kLora + (((lane & 3) ^ ((xr >> 2) & 3)) * 8);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int wr = 64 * wave + 16 * j + (lane >> 2);
+    for (int j = 0; j < WLOADS; ++j) {
+        const int wr = 16 * WLOADS * wave + 16 * j + (lane >> 2);
         w_src[j] = wr * kLora + (((lane & 3) ^ ((wr >> 2) & 3)) * 8);
     }
     const uint16_t* xbase = X + (size_t)m0 * kLora;
@@ -233,7 +245,8 @@ __global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int j = 0; j < 2; ++j) dma16_g(xbase + kc * BK + x_src[j], xdst + (32 * wave + 16 * j) * ROWB);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16_g(wbase + kc * BK + w_src[j], wdst + (64 * wave + 16 * j) * ROWB);
+        for (int j = 0; j < WLOADS; ++j)
+            dma16_g(wbase + kc * BK + w_src[j], wdst + (16 * WLOADS * wave + 16 * j) * ROWB);
     };
 
     f32x16 acc[4][2];
@@ -259,15 +272,17 @@ __global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict
         }
     }
 
+    // Chunks are issued STAGES-1 ahead; the end of chunk kc waits for chunk kc+1 and leaves
+    // the newer ones in flight.
     constexpr int NK = kLora / BK;   // 16 chunks
-    issue(0, xs[0], ws[0]);
-    issue(1, xs[1], ws[1]);
-    __builtin_amdgcn_s_waitcnt(0x3F76);          // vmcnt(6): chunk 0 landed
+#pragma unroll
+    for (int c = 0; c < STAGES - 1; ++c) issue(c, xs[c], ws[c]);
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (LOADS * (STAGES - 2)));   // chunk 0 landed
     barrier_keep_loads();
 #pragma unroll
     for (int kc = 0; kc < NK; ++kc) {
-        const int st = kc % 3;
-        if (kc + 2 < NK) issue(kc + 2, xs[(kc + 2) % 3], ws[(kc + 2) % 3]);
+        const int st = kc % STAGES;
+        if (kc + STAGES - 1 < NK) issue(kc + STAGES - 1, xs[(kc + STAGES - 1) % STAGES], ws[(kc + STAGES - 1) % STAGES]);
         __builtin_amdgcn_sched_barrier(0);       // keep the loads at the top of the chunk
         const uint8_t* xb = xs[st];
         const uint8_t* wb = ws[st];
@@ -283,20 +298,31 @@ __global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict
 #pragma unroll
                 for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
         }
-        // chunk kc+1 must have landed; chunk kc+2's loads may stay in flight
-        if (kc + 2 < NK)
-            __builtin_amdgcn_s_waitcnt(0x3F76);      // vmcnt(6)
-        else
-            __builtin_amdgcn_s_waitcnt(0x3F70);      // vmcnt(0)
+        // chunk kc+1 must have landed; the chunks issued after it may stay in flight
+        {
+            const int newer = min(NK - 1, kc + STAGES - 1) - (kc + 1);
+            if (newer >= 2)
+                __builtin_amdgcn_s_waitcnt(0x3F70 | (LOADS * 2));
+            else if (newer == 1)
+                __builtin_amdgcn_s_waitcnt(0x3F70 | LOADS);
+            else
+                __builtin_amdgcn_s_waitcnt(0x3F70);
+        }
         barrier_keep_loads();
     }
 
     // Epilogue: each wave stages one 32-token x 128-feature block at a time in its own 8 KB of
-    // the (now idle) W ring, rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
+    // the (now idle) ring, rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
     // writes it back as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store).
     // The barrier ending the K loop (after vmcnt(0)) guarantees that no wave still reads the
     // ring and no load into it is in flight.
-    uint8_t* ot = (wave < 2 ? ws0 : ws1) + (wave & 1) * 8192;
+    uint8_t* ot;
+    if (BM == 128) {
+        ot = (wave < 2 ? ws0 : ws1) + (wave & 1) * 8192;
+    } else {
+        const int sl = wave >> 1;                           // 16 KB arrays: two waves each
+        ot = (sl == 0 ? xs0 : sl == 1 ? xs1 : sl == 2 ? xs2 : ws0) + (wave & 1) * 8192;
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -324,9 +350,10 @@ __global__ __launch_bounds__(256) void gemm_up_kernel(const uint16_t* __restrict
 
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
                              hipStream_t stream) {
+    constexpr int BM = UP_BM;
     const int M = B * T;
-    const int mtiles = (M + up2::BM - 1) / up2::BM;
-    gemm_up_kernel<<<mtiles * kHeads, 256, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
+    const int mtiles = (M + BM - 1) / BM;
+    gemm_up_kernel<BM><<<mtiles * kHeads, BM * 2, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
     return hipGetLastError();
 }
 
