@@ -130,18 +130,6 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *reinterpret
 __device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
-__device__ __forceinline__ uint32_t uniform32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-    const uint64_t x = (uint64_t)(size_t)p;
-    return (const void*)(size_t)(((uint64_t)uniform32((uint32_t)(x >> 32)) << 32) | uniform32((uint32_t)x));
-}
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, void* lds) {
-    const uint32_t l = uniform32((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(l)
-                 : "memory", "m0");
-}
 // vmcnt(0): every global->LDS load of this wave has landed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x3F70); }
 
@@ -279,11 +267,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
         for (int k = 0; k < 4; ++k) {
             const int row = 16 * (wave & 3) + 4 * k + r16;
             const int dr = min(row, tl) - row;
-            dma16s(kvh + (size_t)t0 * 256, src_off[k] + (uint32_t)(dr * 512), dst + (16 * (wave & 3) + 4 * k) * 128);
+            dma16(kvh + (size_t)t0 * 256, src_off[k] + (uint32_t)(dr * 512), dst + (16 * (wave & 3) + 4 * k) * 128);
         }
         const int drp = min(kp_row, tl) - kp_row;
-        dma16s(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp + 8 * wave * 64);
-        if (wave < 2) dma16s(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm + wave * kQT);
+        dma16(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp + 8 * wave * 64);
+        if (wave < 2) dma16(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm + wave * kQT);
     };
 
     // ---- per-lane LDS read offsets (bytes).

@@ -4,169 +4,211 @@
 // "DeepSeek-V3.2-Exp · Keys": MHA-prefill excerpt, wkv_b followed by the per-head view).
 //
 // Both operands are K-contiguous, so both feed the 32x32x16 MFMA directly from LDS rows.
-// The kernel computes D^T = W . X^T per 32x32 block: lane l then owns token (l % 32) and four
-// consecutive output features per group of four accumulators, which become one 8-byte store.
-// fp32 accumulation, one rounding to bf16 in the epilogue.
-//
-// Tiling: a 256-thread workgroup (4 waves, WM x WN) owns BM tokens x BN features; K advances in
-// steps of 64 through one LDS stage, the next stage prefetched into registers meanwhile.
+// The kernels compute D^T = W . X^T per 32x32 block: lane l then owns token (l % 32) and four
+// consecutive output features per group of four accumulators. fp32 accumulation, one rounding
+// to bf16 in the epilogue. Both stream K through an LDS ring filled by direct global->LDS loads
+// (no staging registers) and stage the bf16 tile in LDS so global stores write whole row
+// segments.
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
 namespace mla {
 
-enum { kModeDown = 0, kModeUp = 1 };
+// ------------------------------------------------------------------------------------------------
+// Down-projection GEMM: 128 tokens x 192 features per workgroup of four waves (2 x 2, each wave
+// 64 x 96: six 32x32 accumulator blocks). K = 7168 streams in chunks of BK through a STAGES-deep
+// LDS ring filled by direct global->LDS loads. LDS rows are BK*2 bytes; 16-byte chunk c of row r
+// sits at c ^ key(r), key(r) = (r / (256 / rowbytes)) % (rowbytes / 16), so the 16 lanes of an
+// operand read (16 rows, one logical chunk) hit 16 distinct 16-byte bank groups. Within a chunk
+// the operands of k-step s + 1 are read before the MFMAs of step s, and the next chunk's first
+// operands before the last step's MFMAs, so LDS latency hides behind MFMAs. The one barrier per
+// chunk sits before the last step: it makes the next chunk visible and frees the current stage,
+// which is refilled with the chunk STAGES ahead. The epilogue stages the whole bf16 tile in the
+// idle ring and stores 384-byte row segments. Chunks of 64 (128 contiguous bytes of each x row,
+// rows 14 KB apart) rather than 32: with x arriving from HBM rather than the last-level cache,
+// 64-byte pieces made the kernel about a third slower.
+// ------------------------------------------------------------------------------------------------
+#ifndef DOWN_BK
+#define DOWN_BK 64
+#endif
+#ifndef DOWN_STAGES
+#define DOWN_STAGES 3
+#endif
+namespace down {
+constexpr int BM = 128, BN = 192, BK = DOWN_BK, STAGES = DOWN_STAGES;
+constexpr int ROWB = BK * 2;                 // bytes per LDS row
+constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+constexpr int RPL = 64 / CPR;                // rows per 1 KB load
+constexpr int RPG = 256 / ROWB;              // rows per 256-byte bank sweep
+constexpr int XB = BM * ROWB;                // X rows per stage
+constexpr int SB = XB + BN * ROWB;           // bytes per stage
+constexpr int XL = 32 / RPL, WL = 48 / RPL;  // 1 KB loads per wave per chunk (X rows 32w.., W rows 48w..)
+constexpr int LOADS = XL + WL;
+constexpr int KS = BK / 16;                  // MFMA k-steps per chunk
+constexpr int NK = kHidden / BK;
+constexpr int NTILES = kKvAOut / BN;         // 3
+static_assert(NK > STAGES + 1 && STAGES >= 2 && KS >= 2, "ring shape");
+static_assert(STAGES * SB <= 160 * 1024 && STAGES * SB >= BM * 384, "LDS budget");
+__device__ __forceinline__ int key(int r) { return (r / RPG) % CPR; }
+}
 
-constexpr int kBK = 64;
-constexpr int kLdsPad = 8;              // bf16 elements of padding per LDS row
-constexpr int kLdsRow = kBK + kLdsPad;  // 72 elements = 144 bytes
+__global__ __launch_bounds__(256) void gemm_down_kernel(const uint16_t* __restrict__ X,
+                                                        const uint16_t* __restrict__ W, int M,
+                                                        int mtiles, uint16_t* __restrict__ out) {
+    using namespace down;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[STAGES * SB];
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict__ X,
-                                                      const uint16_t* __restrict__ W, int M, int K,
-                                                      int T, int mtiles, int ntiles,
-                                                      uint16_t* __restrict__ out) {
-    static_assert(WM * WN == 4, "four waves");
-    constexpr int WTM = BM / WM, WTN = BN / WN;     // wave tile (tokens, features)
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int CH_X = BM * kBK / 8, CH_W = BN * kBK / 8;   // 16-byte chunks per stage
-    static_assert(CH_X % 256 == 0 && CH_W % 256 == 0, "whole chunks per thread");
-    constexpr int NX = CH_X / 256, NW = CH_W / 256;
-
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * kLdsRow];
-
-    // Tile selection.
-    int mt, nt;
-    const int wg = blockIdx.x;
-    if (MODE == kModeDown) {
-        // The N tiles of one M tile land on the same XCD (workgroups are dealt to the 8 XCDs
-        // round-robin), so the shared X tile is read once per XCD L2.
-        const int xcd = wg & 7, j = wg >> 3;
-        nt = j % ntiles;
-        mt = xcd + 8 * (j / ntiles);
-    } else {
-        // Consecutive workgroups sweep the token tiles of one head; XCD x then sees token tiles
-        // x, x+8, ... for every head, so its X tiles stay L2-resident across heads.
-        nt = wg / mtiles;
-        mt = wg % mtiles;
-    }
-    if (mt >= mtiles || nt >= ntiles) return;
+    // The three N tiles of one M tile land on the same XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the shared X rows are fetched once per XCD L2.
+    const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
+    const int nt = j % NTILES, mt = (j / NTILES) * 8 + xcd;
+    if (mt >= mtiles) return;
     const int m0 = mt * BM, n0 = nt * BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WM, wn = wave / WM;
-
-    // Global addresses of this thread's chunks (rows past M are clamped; their results are
-    // never stored).
-    const uint16_t* xsrc[NX];
-    const uint16_t* wsrc[NW];
-    int xdst[NX], wdst[NW];
+    // DMA: a 1 KB load covers RPL LDS rows; lane i writes row (i / CPR), physical chunk
+    // (i % CPR), which holds logical chunk (i % CPR) ^ key(row). X rows past M are clamped to
+    // M - 1 (never stored).
+    const int pc = lane % CPR;
+    uint32_t x_voff[XL], w_voff[WL];
 #pragma unroll
-    for (int i = 0; i < NX; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-        const int m = min(m0 + row, M - 1);
-        xsrc[i] = X + (size_t)m * K + col;
-        xdst[i] = row * kLdsRow + col;
+    for (int jj = 0; jj < XL; ++jj) {
+        const int r = 32 * wave + RPL * jj + lane / CPR;
+        x_voff[jj] = (uint32_t)((min(m0 + r, M - 1) - m0) * (kHidden * 2) + ((pc ^ key(r)) << 4));
     }
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-        wsrc[i] = W + (size_t)(n0 + row) * K + col;
-        wdst[i] = row * kLdsRow + col;
+    for (int jj = 0; jj < WL; ++jj) {
+        const int r = 48 * wave + RPL * jj + lane / CPR;
+        w_voff[jj] = (uint32_t)(r * (kHidden * 2) + ((pc ^ key(r)) << 4));
     }
-
-    u32x4 xr[NX], wr[NW];
-    auto gload = [&](int k0) {
+    const uint16_t* xg = X + (size_t)m0 * kHidden;
+    const uint16_t* wgp = W + (size_t)n0 * kHidden;
+    auto issue = [&](int kc, uint8_t* st) {
 #pragma unroll
-        for (int i = 0; i < NX; ++i) xr[i] = load16(xsrc[i] + k0);
+        for (int jj = 0; jj < XL; ++jj) dma16(xg + kc * BK, x_voff[jj], st + (32 * wave + RPL * jj) * ROWB);
 #pragma unroll
-        for (int i = 0; i < NW; ++i) wr[i] = load16(wsrc[i] + k0);
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(&Xs[xdst[i]]) = xr[i];
-#pragma unroll
-        for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(&Ws[wdst[i]]) = wr[i];
+        for (int jj = 0; jj < WL; ++jj) dma16(wgp + kc * BK, w_voff[jj], st + XB + (48 * wave + RPL * jj) * ROWB);
     };
 
-    f32x16 acc[FN][FM];
+    // Operand reads: row (l % 32) of a 32-row block, logical chunk 2s + l/32; block row bases
+    // are multiples of 32, so the swizzle key is that of (l % 32) alone.
+    const int fr = lane & 31, fh = lane >> 5, fk = key(fr);
+    const int xrow = (wm * 64 + fr) * ROWB, wrow = XB + (wn * 96 + fr) * ROWB;
+    struct Ops { bf16x8 x[2], w[3]; };
+    auto read_ops = [&](const uint8_t* st, int s, Ops& o) {
+        const int c = ((2 * s + fh) ^ fk) << 4;
 #pragma unroll
-    for (int a = 0; a < FN; ++a)
+        for (int b = 0; b < 2; ++b) o.x[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + xrow + c + b * 32 * ROWB));
 #pragma unroll
-        for (int b = 0; b < FM; ++b) acc[a][b] = f32x16{};
-
-    // LDS read offsets of the MFMA operands: row (l % 32) of each 32-row block, eight
-    // reduction elements chosen by (l / 32).
-    const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-    const int xoff = (wm * WTM + frag_row) * kLdsRow + frag_k;
-    const int woff = (wn * WTN + frag_row) * kLdsRow + frag_k;
-
-    const int nk = K / kBK;
-    gload(0);
-    lstore();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
+        for (int a = 0; a < 3; ++a) o.w[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + wrow + c + a * 32 * ROWB));
+    };
+    f32x16 acc[3][2];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 16) {
-            bf16x8 bx[FM], aw[FN];
+    for (int a = 0; a < 3; ++a)
 #pragma unroll
-            for (int b = 0; b < FM; ++b)
-                bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Xs[xoff + b * 32 * kLdsRow + kk]));
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    auto mma = [&](const Ops& o) {
 #pragma unroll
-            for (int a = 0; a < FN; ++a)
-                aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Ws[woff + a * 32 * kLdsRow + kk]));
+        for (int a = 0; a < 3; ++a)
 #pragma unroll
-            for (int a = 0; a < FN; ++a)
-#pragma unroll
-                for (int b = 0; b < FM; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
+            for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(o.w[a], o.x[b], acc[a][b]);
+    };
+    // vmcnt wait leaving `newer` chunks of this wave's loads in flight.
+    auto wait_newer = [](int newer) {
+        switch (newer) {
+            case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 1)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 2)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 3)); break;
+            default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 4)); break;
         }
-        __syncthreads();
-        if (kt + 1 < nk) {
-            lstore();
-            __syncthreads();
-        }
+    };
+    static_assert(STAGES - 1 <= 5 && LOADS * (STAGES - 1) < 64, "vmcnt range");
+
+    // Prologue: all stages in flight; chunk 0 landed.
+#pragma unroll
+    for (int c = 0; c < STAGES; ++c) issue(c, ring + c * SB);
+    switch (STAGES - 1) {
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 1)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 2)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 3)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 4)); break;
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * 5)); break;
     }
+    barrier_keep_loads();
+    Ops o[2];
+    read_ops(ring, 0, o[0]);
 
-    // Epilogue: lane owns token (l % 32) of each block and features 8*g + 4*(l/32) + 0..3.
+    int rs = 0;   // stage of chunk kc
+    // One chunk: `newer` = chunks issued after kc + 1 that may stay in flight at the barrier;
+    // `refill` issues chunk kc + STAGES into the freed stage; `next` reads chunk kc + 1.
+    auto chunk = [&](int kc, int newer, bool refill, bool next) {
+        uint8_t* cur = ring + rs * SB;
+        const int ns = rs == STAGES - 1 ? 0 : rs + 1;
 #pragma unroll
-    for (int b = 0; b < FM; ++b) {
-        const int m = m0 + wm * WTM + b * 32 + (lane & 31);
-        if (m >= M) continue;
-        uint16_t* dst_row;
-        if (MODE == kModeDown) {
-            dst_row = out + (size_t)m * kKvAOut;
-        } else {
-            const int bb = m / T, t = m - bb * T;
-            dst_row = out + (((size_t)bb * kHeads + nt) * T + t) * 256;   // BN == 256: one head
+        for (int s = 0; s + 1 < KS; ++s) {
+            read_ops(cur, s + 1, o[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);   // these reads go out before the MFMAs
+            mma(o[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        wait_newer(newer);
+        barrier_keep_loads();
+        if (refill) issue(kc + STAGES, cur);
+        if (next) read_ops(ring + ns * SB, 0, o[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(o[(KS - 1) & 1]);
+        rs = ns;
+    };
+    static_assert(((KS - 1) & 1) == 1, "the next chunk's first operands go to o[0]");
+    int kc = 0;
+    for (; kc < NK - STAGES; ++kc) chunk(kc, STAGES - 2, true, true);
+    // Tail: the last STAGES chunks, nothing left to issue.
 #pragma unroll
-        for (int a = 0; a < FN; ++a) {
+    for (int t = 0; t < STAGES; ++t) chunk(kc + t, max(0, STAGES - 2 - t), false, t < STAGES - 1);
+
+    // Epilogue. Every ring read was completed before the last barrier and no load is in flight,
+    // so the ring is free. Tile row r (token) occupies 384 bytes; 16-byte chunk c (features
+    // 8c..8c+7) sits at c ^ (r & 7). Lane owns token (l % 32) of each block and features
+    // 8g + 4(l/32) + 0..3.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int row = wm * 64 + b * 32 + fr;
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = (MODE == kModeDown ? n0 : 0) + wn * WTN + a * 32 + 8 * g + 4 * (lane >> 5);
                 u32x2 v;
                 v[0] = pack_bf16(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
                 v[1] = pack_bf16(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
-                store8(dst_row + n, v);
+                const int c = 12 * wn + 4 * a + g;
+                *reinterpret_cast<u32x2*>(ring + row * 384 + ((c ^ (row & 7)) << 4) + fh * 8) = v;
             }
-        }
+    }
+    __syncthreads();
+    constexpr int NC = BM * 24 / 256;   // 16-byte pieces per thread
+    u32x4 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int idx = i * 256 + tid, row = idx / 24, c = idx - row * 24;
+        v[i] = *reinterpret_cast<const u32x4*>(ring + row * 384 + ((c ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int idx = i * 256 + tid, row = idx / 24, c = idx - row * 24;
+        if (m0 + row < M) store16(out + (size_t)(m0 + row) * kKvAOut + n0 + c * 8, v[i]);
     }
 }
 
 hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, uint16_t* kv_raw,
                                hipStream_t stream) {
-    constexpr int BM = 128, BN = 192;
-    const int mtiles = (M + BM - 1) / BM, ntiles = kKvAOut / BN;
-    const int groups = (mtiles + 7) / 8;
-    const dim3 grid(groups * 8 * ntiles);
-    gemm_nt_kernel<BM, BN, 2, 2, kModeDown><<<grid, 256, 0, stream>>>(x, w_dkv, M, kHidden, 0, mtiles,
-                                                                      ntiles, kv_raw);
+    const int mtiles = (M + down::BM - 1) / down::BM;
+    const dim3 grid(((mtiles + 7) / 8) * 8 * down::NTILES);
+    gemm_down_kernel<<<grid, 256, 0, stream>>>(x, w_dkv, M, mtiles, kv_raw);
     return hipGetLastError();
 }
-
-
 
 // ------------------------------------------------------------------------------------------------
 // Up-projection GEMM, second form: BM tokens x 256 features (one head) per workgroup of BM/32
@@ -194,13 +236,6 @@ __device__ __forceinline__ void dma16_g(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Workgroup barrier without the release fence of __syncthreads(), whose wait would drain every
-// outstanding global->LDS load and so the prefetch ring. This thread's LDS reads are completed
-// first, so no later load into a stage can overtake a read of it; the global->LDS loads that
-// must have landed are waited for explicitly with vmcnt before the barrier.
-__device__ __forceinline__ void barrier_keep_loads() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int BM>
 __global__ __launch_bounds__(BM * 2) void gemm_up_kernel(const uint16_t* __restrict__ X,

@@ -55,6 +55,37 @@ __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_
 __device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void store8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// ---- Direct global->LDS loads issued from inline assembly.
+// dma16(sbase, voff, lds): lane l's 16 bytes at sbase + voff land at LDS address lds + 16 l
+// (global_load_lds_dwordx4, scalar-base form: sbase and the LDS address wave-uniform, voff a
+// 32-bit byte offset per lane; M0 takes the LDS address, one wait state before the load reads
+// it). Issued from assembly so that the compiler's wait bookkeeping does not see it: while such
+// a load may be in flight, the compiler otherwise treats every LDS read as unordered with it and
+// drains all outstanding LDS reads before each use. Every read of a destination therefore waits
+// explicitly (vmcnt of the issuing waves, then a barrier); loads the compiler does not see only
+// make its own vmcnt waits stricter.
+__device__ __forceinline__ uint32_t uniform32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t x = (uint64_t)(size_t)p;
+    return (const void*)(size_t)(((uint64_t)uniform32((uint32_t)(x >> 32)) << 32) | uniform32((uint32_t)x));
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, void* lds) {
+    const uint32_t l = uniform32((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(l)
+                 : "memory", "m0");
+}
+// s_waitcnt immediate for vmcnt(n), n < 64 (bits 3:0 and 15:14), other counters unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// Workgroup barrier without the release fence of __syncthreads(), whose vmcnt(0) would drain
+// loads still meant to be in flight. This thread's LDS reads complete first, so no later load
+// into a buffer can overtake a read of it; loads that must have landed are waited for with vmcnt
+// before the barrier.
+__device__ __forceinline__ void barrier_keep_loads() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
