@@ -9,11 +9,12 @@
 // Two kernels:
 //  * sel_bitmap: the index mask plus causal mask as bits, bitmap[b][t/32][s] bit t%32, shared by
 //    all heads (one bit per (query, key) instead of a T x T float tensor).
-//  * sparse_attn: flash-style attention. One workgroup owns (b, h, a tile of queries); key tiles
-//    of 64 are staged in LDS (K as [key][192], V transposed as [128][key]); a key block that no
-//    query of a wave selects is skipped, selected-but-not-all blocks are scored and masked to
-//    -inf, so masked keys get exactly zero weight. Online softmax in fp32 (running max and sum
-//    per query, base-2 exponentials), bf16 MFMA for q.k and p.v with fp32 accumulation.
+//  * sparse_attn: flash-style attention on a persistent grid (one workgroup per compute unit)
+//    that walks work items (b, h, a tile of 256 queries) in a fixed order; key tiles of 64 are
+//    staged in LDS (key and value rows as stored); every key tile at or before a wave's queries
+//    is scored and keys outside the selection are masked to -inf, so they get exactly zero
+//    weight. Online softmax in fp32 (running max and sum per query, base-2 exponentials), bf16
+//    MFMA for q.k and p.v with fp32 accumulation.
 //
 // MFMA formulation: S^T = K . Q^T (32 keys x 32 queries per block), so lane l owns query
 // (l % 32) and 16 of the block's keys; the row max and row sum are in-lane plus one exchange
@@ -88,7 +89,8 @@ hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout,
 // ------------------------------------------------------------------------------------------------
 // Attention.
 // ------------------------------------------------------------------------------------------------
-// Workgroup: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h).
+// Work item: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h); a workgroup runs
+// its items one after another.
 //
 // Key tiles of 64 keys (two 32-key blocks) rotate through three statically distinct LDS stages
 // filled by direct global->LDS loads; tile kt+2 is loaded while tile kt is computed, and one
@@ -200,26 +202,34 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ kv,
                                                           const uint16_t* __restrict__ kpe,
                                                           const uint32_t* __restrict__ bitmap, int T,
-                                                          int Tpad, int Wp, int nqt, float c2,
-                                                          uint16_t* __restrict__ out) {
+                                                          int Tpad, int Wp, int nqt, int BH, int npairs,
+                                                          int units, float c2, uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t knA[kKT * 128], knB[kKT * 128], knC[kKT * 128];
     __shared__ __attribute__((aligned(16))) uint16_t kpA[kKT * 64], kpB[kKT * 64], kpC[kKT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t vA[kKT * 128], vB[kKT * 128], vC[kKT * 128];
     __shared__ __attribute__((aligned(16))) uint32_t bmA[2 * kQT], bmB[2 * kQT], bmC[2 * kQT];
     const Stage stA{knA, kpA, vA, bmA}, stB{knB, kpB, vB, bmB}, stC{knC, kpC, vC, bmC};
 
-    // Workgroups are dealt to the 8 XCDs round-robin. Every query tile of one (b, h) goes to
-    // the same XCD so the head's keys and values stay in that XCD's L2; within a head the
-    // longest (latest) query tiles start first.
-    const int wg = blockIdx.x;
-    const int xcd = wg & 7, j = wg >> 3;
-    const int bh = xcd + 8 * (j / nqt);
-    const int qt = nqt - 1 - (j % nqt);
-    const int b = bh / kHeads, h = bh - b * kHeads;
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
+
+    // Persistent schedule. A unit is a pair of query tiles of one (b, h): tile nqt-1-p (the
+    // longer) then tile p, so every unit costs about the same number of key tiles. Workgroups
+    // are dealt to the 8 XCDs round-robin, so workgroup w sits on XCD w % 8 and takes the
+    // units u = w, w + G, ... (G a multiple of 8), all of that XCD: unit u covers head
+    // bh = u % 8 + 8 * (k / npairs), pair k % npairs, k = u / 8. The workgroups of one XCD run
+    // the pairs of a few heads side by side and in step, so those heads' keys and values are
+    // shared through that XCD's L2.
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int k_ = u >> 3;
+    const int bh = (u & 7) + 8 * (k_ / npairs);
+    const int pr = k_ - (k_ / npairs) * npairs;
+    if (bh >= BH) continue;
+    const int b = bh / kHeads, h = bh - b * kHeads;
+    for (int item = 0; item < 2; ++item) {
+    const int qt = item == 0 ? nqt - 1 - pr : pr;
+    if (item == 1 && qt == nqt - 1 - pr) break;   // odd count: the middle tile stands alone
     const int q0 = qt * kQT;
     const int wq0 = q0 + wave * kQW;
     const int qrow = wq0 + col;
@@ -392,6 +402,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
                 store8(dst + dt * 32 + 8 * g + 4 * half, v);
             }
     }
+    }   // items of the unit
+    }   // units
 }
 
 int attn_bitmap_words(int T) { return 2 * ((T + kKT - 1) / kKT); }
@@ -401,10 +413,19 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint1
                               const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
                               hipStream_t stream) {
     const int nqt = (T + kQT - 1) / kQT;
+    const int npairs = (nqt + 1) / 2;
+    const int BH = B * kHeads;
+    const int units = 8 * ((BH + 7) / 8) * npairs;     // a multiple of 8
+    // one workgroup per compute unit (the LDS use admits one), a multiple of 8
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n >= 8) cus = n;
+    }
+    const int G = min(units, cus / 8 * 8);
     const float c2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-    const dim3 grid(B * kHeads * nqt);
-    sparse_attn_kernel<<<grid, kWaves * 64, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
-                                                         attn_bitmap_words(T), nqt, c2, out);
+    sparse_attn_kernel<<<G, kWaves * 64, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
+                                                      attn_bitmap_words(T), nqt, BH, npairs, units, c2, out);
     return hipGetLastError();
 }
 
