@@ -193,8 +193,10 @@ def _run_attn(q, kv, kpe, topk, scale=SCALE):
     return to_host(out)
 
 
+# (1, 1100, 300): five query tiles of 256 (an odd count: the middle tile is a unit of its own)
+# and more units than workgroups, so workgroups of the persistent grid take two units.
 @pytest.mark.parametrize("B,T,K", [(1, 64, 16), (2, 200, 48), (1, 1024, 256), (1, 333, 400),
-                                   (1, 1, 1), (3, 130, 7)])
+                                   (1, 1, 1), (3, 130, 7), (1, 1100, 300)])
 def test_attention_matches_oracle(B, T, K):
     say(f"attention B={B} T={T} K={K}")
     q, kv, kpe, topk = _attn_inputs(4000 + T + K, B, T, K)
