@@ -168,6 +168,57 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
                             int B, int T, int K, float softmax_scale, void* out, void* workspace,
                             size_t ws_bytes, void* stream);
 
+/*
+ * Row stride (entries) of the selection lists: ceil(min(T, K) / 64) * 64. Returns 0 for shapes the
+ * list call would reject.
+ */
+int mla_selection_list_stride(int T, int K);
+
+/*
+ * Selection intersected with the causal mask, as sorted lists (the same set as
+ * mla_selection_bitmap: the MHA-prefill excerpt's scattered index mask plus causal mask).
+ *   topk    (device) int32 [B, T, K], as for mla_selection_bitmap.
+ *   lists   (device, out) int32 [B, T, L], L = mla_selection_list_stride(T, K): row (b, s) holds
+ *           the distinct allowed key positions t <= s in increasing order, then 0 up to the next
+ *           multiple of 64 (entries after that are not written).
+ *   counts  (device, out) int32 [B, T]: the number of allowed keys of each row.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_ALIAS, MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_selection_lists(const int32_t* topk, int B, int T, int K, int32_t* lists, int32_t* counts,
+                        void* stream);
+
+/*
+ * Bytes of workspace mla_sparse_prefill_attn_latent needs (a transposed copy of the key half of
+ * W_UKV, the selection lists, the absorbed queries and the latent outputs:
+ * about 16.8 MB + B*T*(4*L + 262152) bytes). Returns 0 for shapes the call would reject.
+ */
+size_t mla_attn_latent_workspace_bytes(int B, int T, int K);
+
+/*
+ * Sparse prefill attention computed in the latent space, for long sequences: the same result as
+ * mla_kv_up followed by mla_sparse_prefill_attn, up to rounding, without forming per-head keys
+ * and values. "DeepSeek-V3.2-Exp · Keys", MHA-prefill code excerpt: per head, the non-rotary key
+ * and the value are the two halves of wkv_b applied to the normalised latent; regrouping the
+ * products (not shown on the pages) scores every head against the shared 576-wide rows
+ * [c_kv | k_pe] of the selected keys only:
+ *   q_lat[h] = bf16(W_UK[h]^T q_nope[h]) (fp32 accumulation), scores = scale * [q_lat | q_pe] . [c_kv | k_pe],
+ *   o_lat[h] = bf16(sum_t softmax_t * c_kv[t]),  out[h] = bf16(W_UV[h] o_lat[h]) (fp32 accumulation),
+ * W_UK[h] = w_ukv rows h*256 .. h*256+127, W_UV[h] = rows h*256+128 .. h*256+255.
+ *   q        (device) bf16 [B, T, 128, 192] as for mla_sparse_prefill_attn.
+ *   c_kv     (device) bf16 [B, T, 512];  k_pe (device) bf16 [B, T, 64] (from mla_kv_latent).
+ *   w_ukv    (device) bf16 [32768, 512] as for mla_kv_up.
+ *   topk     (device) int32 [B, T, K] as for mla_selection_bitmap.
+ *   softmax_scale, out  as for mla_sparse_prefill_attn (out [B, T, 128, 128] bf16).
+ *   workspace, ws_bytes  (device) at least mla_attn_latent_workspace_bytes(B, T, K) bytes,
+ *            contents on entry irrelevant.
+ * Same precondition as mla_sparse_prefill_attn (an empty row yields NaN).
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ARG, MLA_E_ALIAS,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_sparse_prefill_attn_latent(const void* q, const void* c_kv, const void* k_pe, const void* w_ukv,
+                                   const int32_t* topk, int B, int T, int K, float softmax_scale,
+                                   void* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* m^2 / sqrt(192) with m = 1 + 0.1 ln 40, rounded to fp32 ("DeepSeek-V3.2-Exp · Scale scores"). */
 float mla_default_softmax_scale(void);
 

@@ -32,10 +32,11 @@ CFLAGS = [
 
 
 # Extra flags per source file.
-#  attn.hip: -fno-honor-nans lets fmaxf map to plain v_max (no NaN canonicalisation of MFMA
-#  results; the kernels never produce NaN from finite inputs).
+#  attn.hip, latent.hip: -fno-honor-nans lets fmaxf map to plain v_max (no NaN canonicalisation
+#  of MFMA results; the kernels never produce NaN from finite inputs).
 FILE_FLAGS = {
     "attn.hip": ["-fno-honor-nans"],
+    "latent.hip": ["-fno-honor-nans"],
 }
 
 

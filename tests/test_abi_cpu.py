@@ -131,3 +131,40 @@ def test_attention_and_bitmap_validation():
     assert lib.mla_rope_table(0, 10000.0, A, NOSTREAM) == -2
     assert lib.mla_rope_table(8, 10000.0, None, NOSTREAM) == -1
     assert lib.mla_rope_table(8, -1.0, A, NOSTREAM) == -7
+
+
+def test_latent_attention_and_lists_validation():
+    lib = _lib()
+    assert lib.mla_selection_list_stride(4096, 2048) == 2048
+    assert lib.mla_selection_list_stride(100, 2048) == 128
+    assert lib.mla_selection_list_stride(64, 16) == 64
+    assert lib.mla_selection_list_stride(0, 16) == 0
+    ws = lib.mla_attn_latent_workspace_bytes(1, 64, 16)
+    # transposed key weights, then per token: count, flag, list, absorbed query, latent output
+    assert ws >= 128 * 512 * 128 * 2 + 64 * (4 + 4 + 4 * 64 + 2 * 128 * 512 * 2)
+    assert ws % 256 == 0
+    assert lib.mla_attn_latent_workspace_bytes(0, 64, 16) == 0
+    assert lib.mla_attn_latent_workspace_bytes(1, 40000, 16) == 0
+    GB = 1 << 30                        # far apart: the workspace spans tens of MB
+    Q, CKV, KPE, W, TK, OUT, WS = (GB * i for i in range(1, 8))
+
+    def call(q=Q, ckv=CKV, kpe=KPE, w=W, topk=TK, B=1, T=64, K=16, scale=0.135, out=OUT, wk=WS, wsb=ws):
+        return lib.mla_sparse_prefill_attn_latent(q, ckv, kpe, w, topk, B, T, K, scale, out, wk, wsb,
+                                                  NOSTREAM)
+    assert call(q=None) == -1
+    assert call(w=None) == -1
+    assert call(wk=None) == -1
+    assert call(B=0) == -2
+    assert call(T=40000) == -2
+    assert call(ckv=CKV + 2) == -3
+    assert call(wk=WS + 8) == -3
+    assert call(wsb=ws - 1) == -4
+    assert call(scale=-1.0) == -7
+    assert call(out=Q) == -8
+    assert call(wk=W) == -8
+    assert lib.mla_selection_lists(None, 1, 64, 16, OUT, WS, NOSTREAM) == -1
+    assert lib.mla_selection_lists(TK, 1, 64, 16, None, WS, NOSTREAM) == -1
+    assert lib.mla_selection_lists(TK, 1, 0, 16, OUT, WS, NOSTREAM) == -2
+    assert lib.mla_selection_lists(TK, 1, 64, 16, OUT + 4, WS, NOSTREAM) == -3
+    assert lib.mla_selection_lists(TK, 1, 64, 16, TK, WS, NOSTREAM) == -8
+    assert lib.mla_selection_lists(TK, 1, 64, 16, OUT, OUT + 64, NOSTREAM) == -8

@@ -1,0 +1,186 @@
+"""GPU parity of the latent-space attention (mla_sparse_prefill_attn_latent) and of the sorted
+selection lists it runs on, against the CPU oracle.
+
+The latent form regroups the pages' products (queries absorbed into the latent, values mixed in
+the latent), so its reference is the pages' form itself: oracle.kv_up of the latent rows followed
+by oracle.sparse_prefill_attn (or its per-row variant on sampled rows of the full workloads).
+Rounding differs from the pages' order only in where bf16 roundings sit (the absorbed query and
+the latent output instead of the per-head keys and values). Criteria: rel-L2 <= 1e-2 as for the
+head-major path, and per element |got - ref| <= 2e-2 + 2 bf16 steps of |ref|: the head-major
+allowance plus one step for each of the two extra roundings, each of which can move an output
+element by up to about one bf16 step of its own magnitude (the latent output is rounded once and
+then mixed by W_UV, so its error does not average out over keys the way the per-key value
+roundings of the pages' order do). The lists are integer work: bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import assert_within_one_step, bf16_step, dev, fp32_dot_bound, say, to_dev, to_host
+
+mla = pytest.importorskip("sparse_latent_attention_wkv_amd")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a ROCm GPU")]
+
+SCALE = oracle.softmax_scale()
+f32 = synth.bf16_bits_to_f32
+
+
+def attention_close(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    excess = err - (2e-2 + 2 * bf16_step(ref))
+    say(f"  {what}: rel-L2 {rel:.3e}, max-abs {err.max():.3e}, worst margin {excess.max():.3e}")
+    assert rel <= 1e-2, f"{what}: rel-L2 {rel}"
+    assert (excess <= 0).all(), f"{what}: {(excess > 0).sum()} elements beyond 2e-2 + 2 bf16 steps"
+
+
+# ------------------------------------------------------------------------------------ lists
+def _messy_topk(seed, B, T, K):
+    """The workload recipe, then repeated entries, -1 holes, positions past the query and past T."""
+    topk = synth.random_topk(seed, B, T, K)
+    rng = np.random.default_rng(seed)
+    n = topk.size
+    flat = topk.reshape(-1)
+    for frac, fn in ((0.05, lambda k: flat[rng.integers(0, n, k)]),   # duplicates of other entries
+                     (0.05, lambda k: np.full(k, -1)),
+                     (0.03, lambda k: rng.integers(T, T + 50, k)),
+                     (0.03, lambda k: rng.integers(-100, -1, k))):
+        k = int(frac * n)
+        flat[rng.integers(0, n, k)] = fn(k)
+    # entries beyond the query position (removed by the causal mask)
+    s = np.arange(T)[None, :, None]
+    late = rng.random(topk.shape) < 0.05
+    topk[late] = np.minimum(T - 1, s + 1 + rng.integers(0, 5, topk.shape))[late]
+    return topk.astype(np.int32)
+
+
+@pytest.mark.parametrize("B,T,K,messy", [(1, 1, 1, False), (1, 64, 16, False), (2, 300, 40, True),
+                                         (1, 1000, 1000, False), (3, 777, 100, True),
+                                         (1, 4096, 2048, False), (1, 2000, 3000, True)])
+def test_selection_lists(B, T, K, messy):
+    say(f"lists B={B} T={T} K={K} messy={messy}")
+    topk = _messy_topk(900 + T, B, T, K) if messy else synth.random_topk(900 + T, B, T, K)
+    lists, counts = mla.mla_selection_lists(torch.from_numpy(topk).to(dev()))
+    lists, counts = lists.cpu().numpy(), counts.cpu().numpy()
+    allowed = oracle.selection_mask(topk, T)
+    L = lists.shape[2]
+    assert L == (min(T, K) + 63) // 64 * 64
+    for b in range(B):
+        for s in range(T):
+            want = np.nonzero(allowed[b, s])[0]
+            n = len(want)
+            assert counts[b, s] == n, (b, s)
+            assert np.array_equal(lists[b, s, :n], want), (b, s)
+            assert not lists[b, s, n:(n + 63) // 64 * 64].any(), (b, s)
+
+
+# ------------------------------------------------------------------------------------ attention
+def _latent_inputs(seed, B, T, K):
+    q = synth.random_bf16(seed, (B, T, 128, 192))
+    c_kv = synth.random_bf16(seed + 1, (B, T, 512))
+    k_pe = synth.random_bf16(seed + 2, (B, T, 64))
+    w = synth.random_bf16(seed + 3, (32768, 512), std=512 ** -0.5)
+    topk = synth.random_topk(seed + 4, B, T, K)
+    return q, c_kv, k_pe, w, topk
+
+
+def _run_latent(q, c_kv, k_pe, w, topk):
+    out = mla.mla_sparse_prefill_attn_latent(to_dev(q), to_dev(c_kv), to_dev(k_pe), to_dev(w),
+                                             torch.from_numpy(topk).to(dev()), SCALE)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def _oracle(q, c_kv, k_pe, w, topk):
+    kv = oracle.kv_up(f32(c_kv), f32(w))
+    return kv, oracle.sparse_prefill_attn(f32(q), kv, f32(k_pe), topk, SCALE)
+
+
+# (1, 1100, 300): tiles of 32 keys with a ragged last tile for most rows; (1, 333, 400): K > T;
+# (3, 130, 7): several sequences and a top-k below one tile.
+@pytest.mark.parametrize("B,T,K", [(1, 1, 1), (1, 64, 16), (2, 200, 48), (1, 333, 400), (3, 130, 7),
+                                   (1, 1100, 300)])
+def test_latent_attention_matches_oracle(B, T, K):
+    say(f"latent attention B={B} T={T} K={K}")
+    q, c_kv, k_pe, w, topk = _latent_inputs(5000 + T + K, B, T, K)
+    got = _run_latent(q, c_kv, k_pe, w, topk)
+    kv, ref = _oracle(q, c_kv, k_pe, w, topk)
+    attention_close(got, ref, f"latent B{B} T{T} K{K}")
+    # query 0 sees only key 0: the output is W_UV applied to that latent row, i.e. the value row
+    # of the pages' form up to the fp32 summation order
+    wv = f32(w).reshape(128, 256, 512)[:, 128:, :].astype(np.float64)
+    bound = fp32_dot_bound(np.abs(wv) @ np.abs(f32(c_kv)[:, 0].astype(np.float64)).T, 512)   # [128, 128, B]
+    assert_within_one_step(got[:, 0], kv[:, :, 0, 128:], extra=bound.transpose(2, 0, 1), what="query 0")
+
+
+def test_latent_attention_full_selection_is_dense_causal():
+    B, T = 1, 300
+    q, c_kv, k_pe, w, _ = _latent_inputs(5100, B, T, 1)
+    topk = np.tile(np.arange(T, dtype=np.int32), (B, T, 1))
+    got = _run_latent(q, c_kv, k_pe, w, topk)
+    _, ref = _oracle(q, c_kv, k_pe, w, topk)
+    attention_close(got, ref, "latent full selection")
+
+
+def test_latent_attention_exact_max_path():
+    """A key whose scores exceed the first tile's max by far more than 2^64 in weight: the kernel
+    marks those queries and recomputes them with their exact max (no overflow)."""
+    B, T, K = 1, 200, 200
+    q, c_kv, k_pe, w, topk = _latent_inputs(5200, B, T, K)
+    kpe = f32(k_pe)
+    kpe[0, 150] = 60.0                       # rotary part of key 150: scores of order +-60 per unit
+    k_pe = synth.f32_to_bf16_bits(kpe)
+    got = _run_latent(q, c_kv, k_pe, w, topk)
+    _, ref = _oracle(q, c_kv, k_pe, w, topk)
+    attention_close(got, ref, "latent exact-max path")
+
+
+def _latent_rows_ref(q, c_kv, k_pe, w, topk, b, rows):
+    """Oracle for sampled query rows of a large workload: each row's allowed keys alone, as a
+    compact problem (the keys renumbered 0..n-1 in order, the query last)."""
+    res = []
+    wf = f32(w)
+    for s in rows:
+        ids = np.asarray(topk[b, s]).astype(np.int64)
+        ids = np.unique(ids[(ids >= 0) & (ids <= s)])
+        n = len(ids)
+        kv_c = oracle.kv_up(f32(c_kv[b:b + 1, ids]), wf)                     # [1, H, n, 256]
+        q_c = np.zeros((1, n, 128, 192), np.float32)
+        q_c[0, n - 1] = f32(q[b, s])
+        topk_c = np.full((1, n, n), -1, np.int32)
+        topk_c[0, n - 1] = np.arange(n)
+        res.append(oracle.sparse_prefill_attn_rows(q_c, kv_c, f32(k_pe[b:b + 1, ids]), topk_c, SCALE, 0,
+                                                   [n - 1])[0])
+    return np.stack(res)
+
+
+@pytest.mark.parametrize("name", ["headline", "long"])
+def test_latent_workload_sampled(name):
+    w = synth.WORKLOADS[name]
+    say(f"workload {name}: drawing inputs")
+    d = synth.make(w)
+    say(f"workload {name}: front end and latent attention")
+    x, wd, wu, q = to_dev(d["x"]), to_dev(d["w_dkv"]), to_dev(d["w_ukv"]), to_dev(d["q"])
+    gain = torch.from_numpy(d["gain"]).to(dev())
+    topk = torch.from_numpy(d["topk"]).to(dev())
+    _, c_kv, k_pe = mla.mla_kv_latent(x, wd, gain, 1e-6)
+    out = mla.mla_sparse_prefill_attn_latent(q, c_kv, k_pe, wu, topk, SCALE)
+    out2 = mla.mla_sparse_prefill_attn_latent(q, c_kv, k_pe, wu, topk, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "latent attention is not deterministic"
+    ckv_bits = c_kv.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    kpe_bits = k_pe.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng(41)
+    T, K = w.T, w.K
+    for b in range(w.B):
+        rows = sorted(set([0, 1, 31, 32, 33, K - 1, K, T - 1] + rng.integers(0, T, 4).tolist()))
+        say(f"checking {len(rows)} sampled rows of batch {b}")
+        ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], b, rows)
+        attention_close(to_host(out[b, rows]), ref, f"{name} batch {b}")
