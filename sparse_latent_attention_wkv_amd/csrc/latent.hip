@@ -285,7 +285,15 @@ constexpr int KC_BYTES = KT * KC_ROW, KP_BYTES = KT * KP_ROW, STAGE_BYTES = KC_B
 constexpr int QREG = 25;                      // query steps in registers; steps QREG..35 in LDS
 constexpr int QLDS = 36 - QREG;
 constexpr int QROW = QLDS * 32 + 16;          // bytes per head in LDS (16 of padding)
-constexpr int DMAS = 2 * KT / 4;              // gather instructions per wave per tile
+constexpr int DMAS = KT / 4 + 1;              // gather instructions per wave per tile
+#ifndef LAT_RS
+#define LAT_RS 3
+#endif
+#ifndef LAT_RP
+#define LAT_RP 4
+#endif
+constexpr int RS = LAT_RS;                    // score steps of operands in flight
+constexpr int RP = LAT_RP;                    // value MFMAs of operands in flight
 }
 // Score MFMAs with their accumulators in vector registers: every accumulation register of the
 // kernel holds the output block, which the compiler's MFMA form places there, so the score chains
@@ -301,6 +309,14 @@ __device__ __forceinline__ void mfma_vgpr(f32x16& c, const bf16x8& a, const bf16
 }
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16& c0, f32x16& c1) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+// Direct global->LDS load with the LDS address given as a 32-bit LDS byte address (wave-uniform):
+// lane l's 16 bytes at sbase + voff land at lds + 16 l (as dma16).
+__device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
 }
 __device__ __forceinline__ constexpr int lat_sigma(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
@@ -345,18 +361,27 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
     auto load_idx = [&](int kt) __attribute__((always_inline)) {
         iv = *reinterpret_cast<const i32x8*>(lrow + kt * KT + 8 * wave);
     };
-    auto issue = [&](uint8_t* kcs, uint8_t* kps) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+    // instruction j of a tile's gather (DMAS = 9): j < 8 latent row 8w + j, j = 8 the rotary rows
+    // 8w..8w+7 (lane i -> row 8w + i/8, its key position fetched from lane i/8 of a register
+    // holding the eight). LDS destinations are 32-bit LDS addresses (no generic-pointer casts).
+    const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)ring;
+    auto issue_one = [&](uint32_t stage_lds, int j) __attribute__((always_inline)) {
+        if (j < 8) {
             const uint32_t voff = (uint32_t)iv[j] * (uint32_t)KC_ROW + (uint32_t)((lane ^ lat_sigma(8 * wave + j)) << 4);
-            dma16(ckv_b, voff, kcs + (8 * wave + j) * KC_ROW);
-        }
+            dma16_lds(ckv_b, voff, stage_lds + (uint32_t)((8 * wave + j) * KC_ROW));
+        } else {
+            int vi = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = 8 * wave + j;
-            const uint32_t voff = (uint32_t)iv[j] * (uint32_t)KP_ROW + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4);
-            if (lane < 8) dma16(kpe_b, voff, kps + r * KP_ROW);
+            for (int q = 0; q < 8; ++q) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vi) : "s"(iv[q]), "i"(q));
+            const int ip = __builtin_amdgcn_ds_bpermute((lane >> 3) << 2, vi);
+            const int r = 8 * wave + (lane >> 3);
+            const uint32_t voff = (uint32_t)ip * (uint32_t)KP_ROW + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4);
+            dma16_lds(kpe_b, voff, stage_lds + (uint32_t)(KC_BYTES + 8 * wave * KP_ROW));
         }
+    };
+    auto issue = [&](uint32_t stage_lds) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < DMAS; ++j) issue_one(stage_lds, j);
     };
 
     // ---- query fragment (B operand of S^T): lane holds head h, features 16 kc + 8 half .. +7 of
@@ -409,10 +434,14 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
     float m_ref = -INFINITY, l_run = 0.f;
     bool bad = false;
 
-    // S^T of one tile: two MFMA chains (steps 0..17 and 18..35), summed. The operands of step
-    // kc+1 are read before the MFMAs of step kc (scheduling barriers keep that order, so only
-    // two steps of operands are live).
-    auto s_tile = [&](const uint8_t* kcs, const uint8_t* kps) __attribute__((always_inline)) -> f32x16 {
+    // S^T of one tile: two MFMA chains (steps 0..17 and 18..35), summed. With one wave per SIMD
+    // nothing else hides LDS latency, so the operands of step kc + RS - 1 are read before the MFMAs
+    // of step kc (scheduling barriers keep that order and bound the live operands to RS steps).
+    // The gather of a later tile into stage ld_lds is spread over the first DMAS steps, one
+    // instruction per step, so the loads queue behind the MFMAs instead of in one burst.
+    // `piece(kc)` adds independent vector work to step kc (the previous tile's softmax).
+    auto s_tile = [&](const uint8_t* kcs, const uint8_t* kps, uint32_t ld_lds, bool gather, auto&& piece)
+        __attribute__((always_inline)) -> f32x16 {
         f32x16 c0, c1;
         auto a_op = [&](int kc) __attribute__((always_inline)) {
             return kc < 32 ? as_bf16x8(lds16(kcs + kc_off[kc & 7] + 256 * (kc >> 3)))
@@ -421,23 +450,26 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
         auto b_op = [&](int kc) __attribute__((always_inline)) {
             return kc < QREG ? qf[kc < QREG ? kc : 0] : as_bf16x8(lds16(qsl + (kc - QREG) * 32));
         };
-        bf16x8 a[2][2], bq[2][2];
-        a[0][0] = a_op(0); bq[0][0] = b_op(0);
-        a[0][1] = a_op(18); bq[0][1] = b_op(18);
+        bf16x8 a0[RS], a1[RS], b1[RS];
+        auto fetch = [&](int kc) __attribute__((always_inline)) {
+            a0[kc % RS] = a_op(kc);
+            a1[kc % RS] = a_op(kc + 18);
+            b1[kc % RS] = b_op(kc + 18);
+        };
+#pragma unroll
+        for (int kc = 0; kc + 1 < RS; ++kc) fetch(kc);
 #pragma unroll
         for (int kc = 0; kc < 18; ++kc) {
-            const int cur = kc & 1, nx = cur ^ 1;
-            if (kc + 1 < 18) {
-                a[nx][0] = a_op(kc + 1); bq[nx][0] = b_op(kc + 1);
-                a[nx][1] = a_op(kc + 19); bq[nx][1] = b_op(kc + 19);
-            }
+            if (kc + RS - 1 < 18) fetch(kc + RS - 1);
+            if (gather && kc < DMAS) issue_one(ld_lds, kc);
+            piece(kc);
             __builtin_amdgcn_sched_barrier(0);
             if (kc == 0) {
-                mfma_vgpr_first(c0, a[cur][0], bq[cur][0]);
-                mfma_vgpr_first(c1, a[cur][1], bq[cur][1]);
+                mfma_vgpr_first(c0, a0[kc % RS], qf[kc]);
+                mfma_vgpr_first(c1, a1[kc % RS], b1[kc % RS]);
             } else {
-                mfma_vgpr(c0, a[cur][0], bq[cur][0]);
-                mfma_vgpr(c1, a[cur][1], bq[cur][1]);
+                mfma_vgpr(c0, a0[kc % RS], qf[kc]);
+                mfma_vgpr(c1, a1[kc % RS], b1[kc % RS]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -479,6 +511,41 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
         }
         l_run += acc0 + acc1;
     };
+    // The same softmax split into 14 pieces of a few vector instructions, one per score step of
+    // the next tile, so it runs while the matrix core works: pieces 0-3 the max over the lane's
+    // 16 scores, 4 the exchange with lane l ^ 32 and the reference, 5-12 two exponentials each,
+    // 13 the row sum. sv: the tile's masked scores; the probabilities land in pf.
+    f32x16 sv;
+    bf16x8 pf[2];
+    float smx = 0.f, snb = 0.f, sacc0 = 0.f, sacc1 = 0.f;
+    u32x4 spk0, spk1;
+    auto sm_piece = [&](int kc) __attribute__((always_inline)) {
+        if (kc < 4) {
+            const int r = 4 * kc;
+            const float a = fmaxf(fmaxf(sv[r], sv[r + 1]), fmaxf(sv[r + 2], sv[r + 3]));
+            smx = kc == 0 ? a : fmaxf(smx, a);
+        } else if (kc == 4) {
+            const float mt = lane_pair_max(smx) * c2;
+            if (m_ref == -INFINITY) m_ref = mt;    // first tile: it holds a selected key
+            bad = bad || mt > m_ref + 64.0f;
+            snb = -m_ref;
+            sacc0 = 0.f;
+            sacc1 = 0.f;
+        } else if (kc < 13) {
+            const int i = kc - 5;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i], c2, snb));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i + 1], c2, snb));
+            if (i < 4) spk0[i] = pack_bf16(p0, p1); else spk1[i - 4] = pack_bf16(p0, p1);
+            sacc0 += p0;
+            sacc1 += p1;
+        } else if (kc == 13) {
+            l_run += sacc0 + sacc1;
+            pf[0] = as_bf16x8(spk0);
+            pf[1] = as_bf16x8(spk1);
+        }
+    };
+    auto no_piece = [](int) {};
+
     // P.V of one tile: 32 MFMAs into 16 independent accumulators; the operands of MFMA i+1 are
     // read before MFMA i.
     auto pv_tile = [&](const uint8_t* kcs, const bf16x8 pf[2]) __attribute__((always_inline)) {
@@ -489,19 +556,19 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
             const s16x4_l hi = lds_tr8(vb + v_off[dt & 3][1]);
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        bf16x8 av[2];
-        av[0] = v_op(0);
+        // operands read RP MFMAs ahead
+        bf16x8 av[RP];
+#pragma unroll
+        for (int i = 0; i + 1 < RP; ++i) av[i] = v_op(i);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            if (i + 1 < 32) av[(i + 1) & 1] = v_op(i + 1);
+            if (i + RP - 1 < 32) av[(i + RP - 1) % RP] = v_op(i + RP - 1);
             __builtin_amdgcn_sched_barrier(0);
-            o[i & 15] = mfma32x32x16(av[i & 1], pf[i >> 4], o[i & 15]);
+            o[i & 15] = mfma32x32x16(av[i % RP], pf[i >> 4], o[i & 15]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Tile kt in stage `cur`; tile kt+2 is gathered into `ld` (freed by the barrier that ended
-    // tile kt-1), with the key positions loaded one tile earlier.
     // One sweep over the key tiles; OUT: softmax and P.V, else only the running max. The stage
     // of tile kt is kt % 3, a run-time value, so the per-lane LDS offsets exist once (added to
     // the stage base per tile) rather than once per stage. Tile kt+2 is gathered into the stage
@@ -510,40 +577,56 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
         constexpr bool OUT = decltype(out_c)::value;
         if (ntiles > 0) {
             load_idx(0);
-            issue(ring, ring + KC_BYTES);
+            issue(ring_lds);
             if (ntiles > 1) {
                 load_idx(1);
-                issue(ring + STAGE_BYTES, ring + STAGE_BYTES + KC_BYTES);
+                issue(ring_lds + STAGE_BYTES);
             }
             if (ntiles > 2) load_idx(2);
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();   // the query steps in LDS and tiles 0 and 1 are in place
-        int cs = 0;        // stage of tile kt
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const int ls = cs == 0 ? 2 : cs - 1;   // stage of tile kt + 2
-            const uint8_t* kcs = ring + cs * STAGE_BYTES;
-            uint8_t* kcl = ring + ls * STAGE_BYTES;
-            const bool more = kt + 2 < ntiles;
-            if (more) issue(kcl, kcl + KC_BYTES);
-            if (kt + 3 < ntiles) load_idx(kt + 3);
-            f32x16 sc = s_tile(kcs, kcs + KC_BYTES);
-            if (kt == ntiles - 1 && (n & (KT - 1)) != 0) mask_tile(sc, kt * KT);
-            if constexpr (OUT) {
-                bf16x8 pf[2];
-                softmax_tile(sc, pf);
-                pv_tile(kcs, pf);
-            } else {
-                m_ref = fmaxf(m_ref, tile_max(sc));
+        if constexpr (OUT) {
+            // Software pipeline: iteration t computes the scores of tile t+1 with the softmax of
+            // tile t spread over its steps, then P.V of tile t. Tile t+2 is gathered during the
+            // scores into the stage freed by the barrier that ended iteration t-1 and waited for at
+            // the end of the iteration. The scores of "tile ntiles" in the last iteration are
+            // computed on a stage holding valid rows (or, for a one-tile query, unused LDS) and
+            // discarded; past the last tile the gathers repeat the last key positions loaded.
+            if (ntiles > 0) {
+                sv = s_tile(ring, ring + KC_BYTES, 0u, false, no_piece);
+                if (ntiles == 1 && (n & (KT - 1)) != 0) mask_tile(sv, 0);
             }
-            // tile kt+1 must have landed; tile kt+2's gather may stay in flight
-            if (more)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMAS));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            barrier_keep_loads();
-            cs = cs == 2 ? 0 : cs + 1;
+            int cs = 0;    // stage of tile t
+            for (int t = 0; t < ntiles; ++t) {
+                const int ns = cs == 2 ? 0 : cs + 1;   // stage of tile t + 1
+                const int ls = ns == 2 ? 0 : ns + 1;   // stage of tile t + 2
+                const uint8_t* kcs = ring + cs * STAGE_BYTES;
+                const uint8_t* kcn = ring + ns * STAGE_BYTES;
+                f32x16 snext = s_tile(kcn, kcn + KC_BYTES, ring_lds + ls * STAGE_BYTES, true, sm_piece);
+                if (t + 2 == ntiles && (n & (KT - 1)) != 0) mask_tile(snext, (t + 1) * KT);
+                if (t + 3 < ntiles) load_idx(t + 3);
+                pv_tile(kcs, pf);
+                sv = snext;
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile t+2 gathered
+                barrier_keep_loads();
+                cs = ns;
+            }
+        } else {
+            int cs = 0;    // stage of tile kt
+            for (int kt = 0; kt < ntiles; ++kt) {
+                const int ls = cs == 0 ? 2 : cs - 1;   // stage of tile kt + 2
+                const uint8_t* kcs = ring + cs * STAGE_BYTES;
+                f32x16 sc = s_tile(kcs, kcs + KC_BYTES, ring_lds + ls * STAGE_BYTES, true, no_piece);
+                if (kt + 3 < ntiles) load_idx(kt + 3);
+                if (kt == ntiles - 1 && (n & (KT - 1)) != 0) mask_tile(sc, kt * KT);
+                m_ref = fmaxf(m_ref, tile_max(sc));
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMAS));   // tile kt+1 landed
+                barrier_keep_loads();
+                cs = cs == 2 ? 0 : cs + 1;
+            }
         }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no gather left in flight
     };
     if constexpr (EXACT) sweep(std::false_type{});
     sweep(std::true_type{});
