@@ -12,8 +12,10 @@ prices the dominant call (the attention) at its algorithmic work: 640 FLOP per s
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
 `--path latent` replaces the up-projection and the head-major attention by
-mla_sparse_prefill_attn_latent (the latent-space form for long sequences); the roofline keeps the
-same algorithmic unit, and `latent_mfma_flop_per_launch` gives the FLOPs that form executes.
+mla_sparse_prefill_attn_latent (the latent-space form for long sequences), `--path auto` by
+mla_sparse_prefill_attn_auto (head-major rows below the split, latent above); the roofline keeps
+the same algorithmic unit, and `latent_mfma_flop_per_launch` gives the FLOPs the latent form
+executes.
 """
 from __future__ import annotations
 
@@ -161,9 +163,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=["headline", "1k", "long", "tiny"])
-    ap.add_argument("--path", default="head-major", choices=["head-major", "latent"],
+    ap.add_argument("--path", default="head-major", choices=["head-major", "latent", "auto"],
                     help="head-major: mla_kv_up + mla_sparse_prefill_attn; latent: "
-                         "mla_sparse_prefill_attn_latent (no per-head keys and values)")
+                         "mla_sparse_prefill_attn_latent (no per-head keys and values); auto: "
+                         "mla_sparse_prefill_attn_auto (head-major below the split row, latent above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,9 +203,12 @@ def main():
     c_kv = torch.empty((B, T, 512), dtype=torch.bfloat16, device=dev)
     k_pe = torch.empty((B, T, 64), dtype=torch.bfloat16, device=dev)
     latent = args.path == "latent"
-    kv = None if latent else torch.empty((B, 128, T, 256), dtype=torch.bfloat16, device=dev)
+    auto = args.path == "auto"
+    kv = None if (latent or auto) else torch.empty((B, 128, T, 256), dtype=torch.bfloat16, device=dev)
     out = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
-    ws_bytes = mla.mla_attn_latent_workspace_bytes(B, T, K) if latent else mla.mla_attn_workspace_bytes(B, T, K)
+    ws_bytes = (mla.mla_attn_latent_workspace_bytes(B, T, K) if latent else
+                int(mla.lib().mla_attn_auto_workspace_bytes(B, T, K)) if auto else
+                mla.mla_attn_workspace_bytes(B, T, K))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     scale = mla.mla_default_softmax_scale()
     stream = torch.cuda.current_stream(dev)
@@ -213,12 +219,14 @@ def main():
         mla.mla_kv_latent(x, w_dkv, gain, 1e-6, rope_cs, out=(kv_raw, c_kv, k_pe))
         if ev is not None:
             ev[1].record(stream)
-        if not latent:
+        if kv is not None:
             mla.mla_kv_up(c_kv, w_ukv, out=kv)
         if ev is not None:
             ev[2].record(stream)
         if latent:
             mla.mla_sparse_prefill_attn_latent(q, c_kv, k_pe, w_ukv, topk, scale, workspace=ws, out=out)
+        elif auto:
+            mla.mla_sparse_prefill_attn_auto(q, c_kv, k_pe, w_ukv, topk, scale, workspace=ws, out=out)
         else:
             mla.mla_sparse_prefill_attn(q, kv, k_pe, topk, scale, workspace=ws, out=out)
         if ev is not None:
@@ -257,7 +265,7 @@ def main():
     flop_up = 2.0 * B * T * 512 * 32768
     tokens = B * T
     # the counter records were taken on the headline workload (head-major path) only
-    headline = args.workload == "headline" and not latent
+    headline = args.workload == "headline" and args.path == "head-major"
     traffic = traffic_record("sparse_attn") if headline else None
 
     res = {
@@ -275,18 +283,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"sparse MLA prefill {args.workload}: B={B}, T={T}, top-k {K}, "
                                "128 heads, qk 192 / v 128, hidden 7168, latent 512+64"
-                               + (", latent-space attention" if latent else ""),
+                               + (", latent-space attention" if latent else "")
+                               + (f", split form (latent from row {mla.mla_attn_auto_split(T, K)})" if auto else ""),
                    "B": B, "T": T, "top_k": K, "heads": 128, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
                      "kernel": ("mla_sparse_prefill_attn_latent call (lists, absorbed-query GEMM, "
                                 "latent attention, value GEMM)" if latent else
+                                "mla_sparse_prefill_attn_auto call (head-major below the split, "
+                                "latent form above)" if auto else
                                 "mla_sparse_prefill_attn call (sel_bitmap + sparse_attn kernels)"),
                      "algorithmic_flop_per_launch": attn_flop},
         "stages_ms": {"kv_latent": lat, "kv_up": upm, "sparse_attn": att, "gpu_step": gpu_step},
         "stage_tflops": {"kv_latent": flop_down / (lat * 1e-3) / 1e12,
-                         "kv_up": None if latent else flop_up / (upm * 1e-3) / 1e12},
+                         "kv_up": None if kv is None else flop_up / (upm * 1e-3) / 1e12},
         "attention_only_tokens_per_s": tokens / (att * 1e-3),
         "attention_mfma_busy_frac": mfma_busy_record() if headline else None,
         "bandwidth_kernels": side,

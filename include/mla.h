@@ -219,6 +219,30 @@ int mla_sparse_prefill_attn_latent(const void* q, const void* c_kv, const void* 
                                    const int32_t* topk, int B, int T, int K, float softmax_scale,
                                    void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * First query row mla_sparse_prefill_attn_auto hands to the latent form: min(T, 4K) rounded down
+ * to a multiple of 256 (T: every row takes the head-major path). -1 for rejected shapes.
+ */
+int mla_attn_auto_split(int T, int K);
+
+/* Bytes of workspace mla_sparse_prefill_attn_auto needs (0 for rejected shapes). */
+size_t mla_attn_auto_workspace_bytes(int B, int T, int K);
+
+/*
+ * The same attention from the latent rows, split by query position: rows s < split
+ * (mla_attn_auto_split) take the head-major form — per-head keys and values of rows < split, as
+ * mla_kv_up computes them, then the same kernels as mla_sparse_prefill_attn — and rows s >= split
+ * the latent form of mla_sparse_prefill_attn_latent. Under causality a query below split never
+ * sees a key at or above it, so each part is the pages' computation on its rows ("DeepSeek-V3.2-Exp
+ * · Keys", MHA-prefill excerpt). The head-major cost of a query grows with its position (every
+ * causal key tile is scored) while the latent cost is set by the top-k; split is where they meet.
+ * Arguments, results and errors as for mla_sparse_prefill_attn_latent, with the workspace from
+ * mla_attn_auto_workspace_bytes.
+ */
+int mla_sparse_prefill_attn_auto(const void* q, const void* c_kv, const void* k_pe, const void* w_ukv,
+                                 const int32_t* topk, int B, int T, int K, float softmax_scale, void* out,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
 /* m^2 / sqrt(192) with m = 1 + 0.1 ln 40, rounded to fp32 ("DeepSeek-V3.2-Exp · Scale scores"). */
 float mla_default_softmax_scale(void);
 

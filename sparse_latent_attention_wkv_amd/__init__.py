@@ -35,6 +35,9 @@ _SIGS = {
     "mla_selection_lists": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "mla_attn_latent_workspace_bytes": (_SZ, [_I, _I, _I]),
     "mla_sparse_prefill_attn_latent": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP, _SZ, _VP]),
+    "mla_attn_auto_split": (_I, [_I, _I]),
+    "mla_attn_auto_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "mla_sparse_prefill_attn_auto": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP, _SZ, _VP]),
     "mla_default_softmax_scale": (_F, []),
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_last_hip_error": (_I, []),
@@ -274,6 +277,43 @@ def mla_sparse_prefill_attn_latent(q, c_kv, k_pe, w_ukv, topk, softmax_scale: fl
     _need(out, "out", torch.bfloat16, (B, T, HEADS, V_HEAD))
     with torch.cuda.device(q.device):
         _check(lib().mla_sparse_prefill_attn_latent(
+            _ptr(q), _ptr(c_kv), _ptr(k_pe), _ptr(w_ukv), _ptr(topk), B, T, K, softmax_scale,
+            _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(q.device)))
+    return out
+
+
+def mla_attn_auto_split(T: int, K: int) -> int:
+    return int(lib().mla_attn_auto_split(T, K))
+
+
+def mla_sparse_prefill_attn_auto(q, c_kv, k_pe, w_ukv, topk, softmax_scale: float | None = None,
+                                 workspace=None, out=None):
+    """As mla_sparse_prefill_attn_latent, with query rows below mla_attn_auto_split(T, K) taking
+    the head-major form."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, 128, 192]")
+    B, T = q.shape[0], q.shape[1]
+    _need(q, "q", torch.bfloat16, (B, T, HEADS, QK_HEAD))
+    _need(c_kv, "c_kv", torch.bfloat16, (B, T, KV_LORA))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
+    _need(w_ukv, "w_ukv", torch.bfloat16, (KV_B_OUT, KV_LORA))
+    if topk.dim() != 3 or topk.shape[:2] != (B, T):
+        raise ValueError("topk must be [B, T, K]")
+    _need(topk, "topk", torch.int32)
+    K = topk.shape[2]
+    if softmax_scale is None:
+        softmax_scale = mla_default_softmax_scale()
+    need = int(lib().mla_attn_auto_workspace_bytes(B, T, K))
+    if need == 0:
+        raise MLAError("unsupported attention shape")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, HEADS, V_HEAD), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, HEADS, V_HEAD))
+    with torch.cuda.device(q.device):
+        _check(lib().mla_sparse_prefill_attn_auto(
             _ptr(q), _ptr(c_kv), _ptr(k_pe), _ptr(w_ukv), _ptr(topk), B, T, K, softmax_scale,
             _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(q.device)))

@@ -52,14 +52,16 @@ __device__ __forceinline__ float lane_pair_sum(float v) {
 int latent_list_stride(int T, int K) { return (min(T, K) + 63) / 64 * 64; }
 
 // QR query rows per workgroup: their allowed sets as bitmap rows in LDS (the same set semantics
-// as the dense mask), then one wave per row turns its bitmap into the ascending list.
+// as the dense mask), then one wave per row turns its bitmap into the ascending list. Rows
+// s_lo..T-1 of each sequence; row s of sequence b is output row b*(T - s_lo) + s - s_lo.
 template <int QR>
-__global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict__ topk, int T, int K,
+__global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict__ topk, int T, int K, int s_lo,
                                                        int Lp, int32_t* __restrict__ lists,
                                                        int32_t* __restrict__ counts) {
     extern __shared__ uint32_t bits_lds[];
     const int Wd = (T + 31) / 32, WP = Wd + 1;
-    const int s0 = blockIdx.x * QR, b = blockIdx.y;
+    const int Tr = T - s_lo;
+    const int s0 = s_lo + blockIdx.x * QR, b = blockIdx.y;
     const int nrows = max(0, min(QR, T - s0));
     for (int i = threadIdx.x; i < QR * WP; i += 256) bits_lds[i] = 0;
     __syncthreads();
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict
     for (int qi = wave; qi < nrows; qi += 4) {
         const int s = s0 + qi;
         const uint32_t* row = bits_lds + qi * WP;
-        int32_t* dst = lists + ((size_t)b * T + s) * Lp;
+        const size_t orow = (size_t)b * Tr + (s - s_lo);
+        int32_t* dst = lists + orow * Lp;
         const int nw = (s >> 5) + 1;             // words that can hold keys <= s
         int total = 0;
         for (int c = 0; c < nw; c += 64) {
@@ -99,17 +102,22 @@ __global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict
         }
         const int padded = (total + 63) & ~63;
         for (int p = total + lane; p < padded; p += 64) dst[p] = 0;
-        if (lane == 0) counts[(size_t)b * T + s] = total;
+        if (lane == 0) counts[orow] = total;
     }
+}
+
+static hipError_t launch_sel_list_range(const int32_t* topk, int B, int T, int K, int s_lo, int32_t* lists,
+                                        int32_t* counts, hipStream_t stream) {
+    constexpr int QR = 8;
+    const dim3 grid((T - s_lo + QR - 1) / QR, B);
+    const size_t lds = (size_t)QR * ((T + 31) / 32 + 1) * sizeof(uint32_t);
+    sel_list_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, s_lo, latent_list_stride(T, K), lists, counts);
+    return hipGetLastError();
 }
 
 hipError_t launch_sel_list(const int32_t* topk, int B, int T, int K, int32_t* lists, int32_t* counts,
                            hipStream_t stream) {
-    constexpr int QR = 8;
-    const dim3 grid((T + QR - 1) / QR, B);
-    const size_t lds = (size_t)QR * ((T + 31) / 32 + 1) * sizeof(uint32_t);
-    sel_list_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, latent_list_stride(T, K), lists, counts);
-    return hipGetLastError();
+    return launch_sel_list_range(topk, B, T, K, 0, lists, counts, stream);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -320,14 +328,16 @@ __device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint
 }
 __device__ __forceinline__ constexpr int lat_sigma(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
+// Queries s_lo..T-1 of every sequence; query row r = b*(T - s_lo) + s - s_lo indexes the
+// per-row buffers (M = B*(T - s_lo) rows).
 struct LatArgs {
     const uint16_t* qlat;    // [M][128][512]
-    const uint16_t* q;       // [M][128][192], rotary part used
+    const uint16_t* q;       // [B][T][128][192], rotary part used
     const uint16_t* ckv;     // [B][T][512]
     const uint16_t* kpe;     // [B][T][64]
     const int32_t* lists;    // [M][Lp]
     const int32_t* counts;   // [M]
-    int T, M, Lp;
+    int T, M, Lp, s_lo;
     float c2;                // softmax scale * log2(e)
     uint16_t* olat;          // [128][M][512]
 };
@@ -344,7 +354,9 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
-    const int b = m / T;
+    const int Tr = T - A.s_lo;
+    const int b = m / Tr;
+    const int tok = b * T + A.s_lo + (m - b * Tr);     // global token index of query row m
     const int n = A.counts[m];
     const int ntiles = (n + KT - 1) / KT;
     const int h = wave * 32 + col;
@@ -389,7 +401,7 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
     bf16x8 qf[QREG];
     {
         const uint16_t* ql = A.qlat + ((size_t)m * kHeads + h) * kLora + half * 8;
-        const uint16_t* qp = A.q + ((size_t)m * kHeads + h) * kQkHead + kNope + half * 8;
+        const uint16_t* qp = A.q + ((size_t)tok * kHeads + h) * kQkHead + kNope + half * 8;
         auto qsrc = [&](int kc) __attribute__((always_inline)) { return kc < 32 ? ql + kc * 16 : qp + (kc - 32) * 16; };
 #pragma unroll
         for (int kc = 0; kc < QREG; ++kc) qf[kc] = as_bf16x8(load16(qsrc(kc)));
@@ -651,16 +663,18 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
 #define LAT_KERNEL_ARGS                                                                           \
     const uint16_t *__restrict__ qlat, const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv, \
         const uint16_t *__restrict__ kpe, const int32_t *__restrict__ lists,                            \
-        const int32_t *__restrict__ counts, int T, int M, int Lp, float c2, uint16_t *__restrict__ olat
-#define LAT_ARGS_STRUCT LatArgs A{qlat, q, ckv, kpe, lists, counts, T, M, Lp, c2, olat}
+        const int32_t *__restrict__ counts, int T, int M, int Lp, int s_lo, float c2,                   \
+        uint16_t *__restrict__ olat
+#define LAT_ARGS_STRUCT LatArgs A{qlat, q, ckv, kpe, lists, counts, T, M, Lp, s_lo, c2, olat}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_latent_kernel(LAT_KERNEL_ARGS, int32_t* __restrict__ flags) {
     LAT_ARGS_STRUCT;
     __shared__ __attribute__((aligned(16))) uint8_t ring[lat::STAGES * lat::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t qs[kHeads * lat::QROW];
-    const int b = blockIdx.x / A.T, s = A.T - 1 - (blockIdx.x - b * A.T);
-    const int m = b * A.T + s;
+    const int Tr = A.T - A.s_lo;
+    const int b = blockIdx.x / Tr, i = blockIdx.x - b * Tr;
+    const int m = b * Tr + (Tr - 1 - i);       // later queries (more keys) first
     const bool bad = attn_latent_query<false>(A, m, ring, qs);
     if (threadIdx.x == 0) flags[m] = bad ? 1 : 0;
 }
@@ -689,9 +703,9 @@ void attn_latent_exact_kernel(LAT_KERNEL_ARGS, const int32_t* __restrict__ flags
 // ------------------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-LatentWorkspace latent_workspace(int B, int T, int K) {
+LatentWorkspace latent_workspace(int B, int T, int K, int s_lo) {
     LatentWorkspace w;
-    const size_t M = (size_t)B * T;
+    const size_t M = (size_t)B * (T - s_lo);
     const int Lp = latent_list_stride(T, K);
     size_t off = 0;
     w.wukT = off;   off += align256((size_t)kHeads * kLora * kNope * 2);
@@ -705,9 +719,9 @@ LatentWorkspace latent_workspace(int B, int T, int K) {
 }
 
 hipError_t launch_sparse_attn_latent(const uint16_t* q, const uint16_t* c_kv, const uint16_t* k_pe,
-                                     const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K,
+                                     const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K, int s_lo,
                                      float scale, uint16_t* out, void* workspace, hipStream_t stream) {
-    const LatentWorkspace w = latent_workspace(B, T, K);
+    const LatentWorkspace w = latent_workspace(B, T, K, s_lo);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     uint16_t* wukT = reinterpret_cast<uint16_t*>(ws + w.wukT);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
@@ -715,31 +729,28 @@ hipError_t launch_sparse_attn_latent(const uint16_t* q, const uint16_t* c_kv, co
     int32_t* lists = reinterpret_cast<int32_t*>(ws + w.lists);
     uint16_t* qlat = reinterpret_cast<uint16_t*>(ws + w.qlat);
     uint16_t* olat = reinterpret_cast<uint16_t*>(ws + w.olat);
-    const int M = B * T;
+    const int Tr = T - s_lo;
+    const int M = B * Tr;
     const int Lp = latent_list_stride(T, K);
 
-    hipError_t e = launch_sel_list(topk, B, T, K, lists, counts, stream);
+    hipError_t e = launch_sel_list_range(topk, B, T, K, s_lo, lists, counts, stream);
     if (e != hipSuccess) return e;
     wuk_t_kernel<<<dim3(kLora / 64, kNope / 64, kHeads), 256, 0, stream>>>(w_ukv, wukT);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // q_lat[m][h][n] = sum_j q[m][h][j] W_UK[h][j][n]
-    {
+    // q_lat[r][h][n] = sum_j q[b][s][h][j] W_UK[h][j][n], one launch per sequence (rows s_lo..T-1)
+    for (int b = 0; b < B; ++b) {
         constexpr int BM = 128, BN = 256;
-        const int mtiles = (M + BM - 1) / BM, ntiles = kLora / BN;
+        const int mtiles = (Tr + BM - 1) / BM, ntiles = kLora / BN;
         gemm_heads_kernel<BM, BN, kNope><<<mtiles * ntiles * kHeads, BM * BN / 128, 0, stream>>>(
-            q, (size_t)kHeads * kQkHead, kQkHead, wukT, (size_t)kLora * kNope, M, mtiles, ntiles, qlat,
+            q + ((size_t)b * T + s_lo) * kHeads * kQkHead, (size_t)kHeads * kQkHead, kQkHead, wukT,
+            (size_t)kLora * kNope, Tr, mtiles, ntiles, qlat + (size_t)b * Tr * kHeads * kLora,
             (size_t)kHeads * kLora, kLora);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    LatArgs la;
-    la.qlat = qlat; la.q = q; la.ckv = c_kv; la.kpe = k_pe; la.lists = lists; la.counts = counts;
-    la.T = T; la.M = M; la.Lp = Lp;
-    la.c2 = (float)((double)scale * 1.4426950408889634);
-    la.olat = olat;
-    attn_latent_kernel<<<M, 256, 0, stream>>>(la.qlat, la.q, la.ckv, la.kpe, la.lists, la.counts, la.T, la.M,
-                                              la.Lp, la.c2, la.olat, flags);
+    const float c2 = (float)((double)scale * 1.4426950408889634);
+    attn_latent_kernel<<<M, 256, 0, stream>>>(qlat, q, c_kv, k_pe, lists, counts, T, M, Lp, s_lo, c2, olat, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         int dev = 0, cus = 256;
@@ -748,21 +759,83 @@ hipError_t launch_sparse_attn_latent(const uint16_t* q, const uint16_t* c_kv, co
             if (hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && nc > 0) cus = nc;
         }
         const int blocks = min(cus, (M + 63) / 64);
-        attn_latent_exact_kernel<<<blocks, 256, 0, stream>>>(la.qlat, la.q, la.ckv, la.kpe, la.lists, la.counts,
-                                                             la.T, la.M, la.Lp, la.c2, la.olat, flags);
+        attn_latent_exact_kernel<<<blocks, 256, 0, stream>>>(qlat, q, c_kv, k_pe, lists, counts, T, M, Lp, s_lo, c2,
+                                                             olat, flags);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    // out[m][h][d] = sum_n o_lat[h][m][n] W_UV[h][d][n], W_UV[h] = rows h*256 + 128 + d
-    {
+    // out[b][s][h][d] = sum_n o_lat[h][r][n] W_UV[h][d][n], W_UV[h] = rows h*256 + 128 + d
+    for (int b = 0; b < B; ++b) {
         constexpr int BM = 256, BN = 128;
-        const int mtiles = (M + BM - 1) / BM;
+        const int mtiles = (Tr + BM - 1) / BM;
         gemm_heads_kernel<BM, BN, kLora><<<mtiles * kHeads, BM * BN / 128, 0, stream>>>(
-            olat, kLora, (size_t)M * kLora, w_ukv + (size_t)kNope * kLora, (size_t)256 * kLora, M, mtiles, 1,
-            out, (size_t)kHeads * kVHead, kVHead);
+            olat + (size_t)b * Tr * kLora, kLora, (size_t)M * kLora, w_ukv + (size_t)kNope * kLora,
+            (size_t)256 * kLora, Tr, mtiles, 1, out + ((size_t)b * T + s_lo) * kHeads * kVHead,
+            (size_t)kHeads * kVHead, kVHead);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Split form for long sequences: queries 0..split-1 of each sequence through the head-major path
+// (their keys and values formed per head, only for rows < split), queries split..T-1 through the
+// latent form. The head-major cost of query s grows with s (all causal tiles are scored) while
+// the latent cost is fixed by the top-k; measured on the long workload the two meet near
+// s = 3.9 K, so split = min(T, 4 K) rounded down to a multiple of 256.
+// ------------------------------------------------------------------------------------------------
+#ifndef LAT_SPLIT_X4
+#define LAT_SPLIT_X4 16   // split = (LAT_SPLIT_X4 / 4) * K
+#endif
+int latent_auto_split(int T, int K) {
+    const long long s = ((long long)LAT_SPLIT_X4 * K / 4) / 256 * 256;
+    return s >= T ? T : (int)s;
+}
+
+// When every row takes the head-major path (split = T) its buffers hold all B sequences and the
+// calls are batched; otherwise one sequence's buffers are reused for each sequence in turn.
+AutoWorkspace auto_workspace(int B, int T, int K) {
+    AutoWorkspace a;
+    a.split = latent_auto_split(T, K);
+    const size_t nseq = a.split == T ? (size_t)B : 1;
+    size_t off = 0;
+    a.kv = off;       off += align256(nseq * kHeads * a.split * 256 * 2);
+    a.bitmap = off;   off += align256(nseq * attn_bitmap_words(a.split) * attn_bitmap_cols(a.split) * 4);
+    a.latent = off;   off += a.split < T ? latent_workspace(B, T, K, a.split).bytes : 0;
+    a.bytes = off;
+    return a;
+}
+
+hipError_t launch_sparse_attn_auto(const uint16_t* q, const uint16_t* c_kv, const uint16_t* k_pe,
+                                   const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K, float scale,
+                                   uint16_t* out, void* workspace, hipStream_t stream) {
+    const AutoWorkspace a = auto_workspace(B, T, K);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint16_t* kvp = reinterpret_cast<uint16_t*>(ws + a.kv);
+    uint32_t* bm = reinterpret_cast<uint32_t*>(ws + a.bitmap);
+    hipError_t e = hipSuccess;
+    if (a.split == T) {   // the head-major path for every row, all sequences at once
+        if ((e = launch_gemm_kv_up(c_kv, w_ukv, B, T, kvp, stream)) != hipSuccess) return e;
+        if ((e = launch_sel_bitmap(topk, B, T, K, attn_bitmap_words(T), attn_bitmap_cols(T), bm, stream)) !=
+            hipSuccess)
+            return e;
+        return launch_sparse_attn(q, kvp, k_pe, bm, B, T, scale, out, stream);
+    }
+    // rows 0..split-1 of sequence b are a contiguous prefix of each per-token tensor, so each
+    // sequence's prefix is a one-sequence problem of length split; kv and bitmap are reused
+    for (int b = 0; b < B && a.split > 0; ++b) {
+        const int S = a.split;
+        if ((e = launch_gemm_kv_up(c_kv + (size_t)b * T * kLora, w_ukv, 1, S, kvp, stream)) != hipSuccess) return e;
+        if ((e = launch_sel_bitmap(topk + (size_t)b * T * K, 1, S, K, attn_bitmap_words(S), attn_bitmap_cols(S), bm,
+                                   stream)) != hipSuccess)
+            return e;
+        if ((e = launch_sparse_attn(q + (size_t)b * T * kHeads * kQkHead, kvp, k_pe + (size_t)b * T * kRope, bm, 1, S,
+                                    scale, out + (size_t)b * T * kHeads * kVHead, stream)) != hipSuccess)
+            return e;
+    }
+    if (a.split < T)
+        e = launch_sparse_attn_latent(q, c_kv, k_pe, w_ukv, topk, B, T, K, a.split, scale, out, ws + a.latent, stream);
+    return e;
 }
 
 }  // namespace mla

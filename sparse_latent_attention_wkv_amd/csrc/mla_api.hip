@@ -248,7 +248,7 @@ int mla_selection_lists(const int32_t* topk, int B, int T, int K, int32_t* lists
 
 size_t mla_attn_latent_workspace_bytes(int B, int T, int K) {
     if (validate_topk(reinterpret_cast<const int32_t*>(16), B, T, K) != MLA_OK) return 0;
-    return mla::latent_workspace(B, T, K).bytes;
+    return mla::latent_workspace(B, T, K, 0).bytes;
 }
 
 int mla_sparse_prefill_attn_latent(const void* q, const void* c_kv, const void* k_pe, const void* w_ukv,
@@ -261,7 +261,7 @@ int mla_sparse_prefill_attn_latent(const void* q, const void* c_kv, const void* 
         !aligned16(workspace))
         return MLA_E_ALIGN;
     if (!pos_finite(softmax_scale)) return MLA_E_ARG;
-    const size_t need = mla::latent_workspace(B, T, K).bytes;
+    const size_t need = mla::latent_workspace(B, T, K, 0).bytes;
     if (ws_bytes < need) return MLA_E_WORKSPACE;
     const size_t M = (size_t)B * T;
     const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
@@ -273,6 +273,43 @@ int mla_sparse_prefill_attn_latent(const void* q, const void* c_kv, const void* 
     if (any_alias(outs, 2, ins, 5)) return MLA_E_ALIAS;
     if ((st = check_device()) != MLA_OK) return st;
     return launched(mla::launch_sparse_attn_latent(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(k_pe),
+        static_cast<const uint16_t*>(w_ukv), topk, B, T, K, 0, softmax_scale, static_cast<uint16_t*>(out), workspace,
+        static_cast<hipStream_t>(stream)));
+}
+
+int mla_attn_auto_split(int T, int K) {
+    if (validate_topk(reinterpret_cast<const int32_t*>(16), 1, T, K) != MLA_OK) return -1;
+    return mla::latent_auto_split(T, K);
+}
+
+size_t mla_attn_auto_workspace_bytes(int B, int T, int K) {
+    if (validate_topk(reinterpret_cast<const int32_t*>(16), B, T, K) != MLA_OK) return 0;
+    return mla::auto_workspace(B, T, K).bytes;
+}
+
+int mla_sparse_prefill_attn_auto(const void* q, const void* c_kv, const void* k_pe, const void* w_ukv,
+                                 const int32_t* topk, int B, int T, int K, float softmax_scale, void* out,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!q || !c_kv || !k_pe || !w_ukv || !out || !workspace) return MLA_E_NULL;
+    if (!aligned16(q) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_ukv) || !aligned16(out) ||
+        !aligned16(workspace))
+        return MLA_E_ALIGN;
+    if (!pos_finite(softmax_scale)) return MLA_E_ARG;
+    const size_t need = mla::auto_workspace(B, T, K).bytes;
+    if (ws_bytes < need) return MLA_E_WORKSPACE;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
+                        {c_kv, M * MLA_KV_LORA * kBf16},
+                        {k_pe, M * MLA_ROPE * kBf16},
+                        {w_ukv, (size_t)MLA_KV_B_OUT * MLA_KV_LORA * kBf16},
+                        {topk, M * K * sizeof(int32_t)}};
+    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}, {workspace, need}};
+    if (any_alias(outs, 2, ins, 5)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_sparse_attn_auto(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(k_pe),
         static_cast<const uint16_t*>(w_ukv), topk, B, T, K, softmax_scale, static_cast<uint16_t*>(out), workspace,
         static_cast<hipStream_t>(stream)));

@@ -26,16 +26,27 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint1
                               hipStream_t stream);
 
 
-// Latent-space attention (long sequences): selection lists, workspace layout, launch sequence.
+// Latent-space attention (long sequences): selection lists, workspace layout, launch sequence
+// for the queries s_lo..T-1 of every sequence.
 int latent_list_stride(int T, int K);
 hipError_t launch_sel_list(const int32_t* topk, int B, int T, int K, int32_t* lists, int32_t* counts,
                            hipStream_t stream);
 struct LatentWorkspace {
     size_t wukT, counts, flags, lists, qlat, olat, bytes;   // byte offsets into the workspace, total
 };
-LatentWorkspace latent_workspace(int B, int T, int K);
+LatentWorkspace latent_workspace(int B, int T, int K, int s_lo);
 hipError_t launch_sparse_attn_latent(const uint16_t* q, const uint16_t* c_kv, const uint16_t* k_pe,
-                                     const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K,
+                                     const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K, int s_lo,
                                      float scale, uint16_t* out, void* workspace, hipStream_t stream);
+// Split form: head-major for queries < split, latent form for the rest.
+int latent_auto_split(int T, int K);
+struct AutoWorkspace {
+    int split;
+    size_t kv, bitmap, latent, bytes;
+};
+AutoWorkspace auto_workspace(int B, int T, int K);
+hipError_t launch_sparse_attn_auto(const uint16_t* q, const uint16_t* c_kv, const uint16_t* k_pe,
+                                   const uint16_t* w_ukv, const int32_t* topk, int B, int T, int K, float scale,
+                                   uint16_t* out, void* workspace, hipStream_t stream);
 
 }  // namespace mla

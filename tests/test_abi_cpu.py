@@ -168,3 +168,28 @@ def test_latent_attention_and_lists_validation():
     assert lib.mla_selection_lists(TK, 1, 64, 16, OUT + 4, WS, NOSTREAM) == -3
     assert lib.mla_selection_lists(TK, 1, 64, 16, TK, WS, NOSTREAM) == -8
     assert lib.mla_selection_lists(TK, 1, 64, 16, OUT, OUT + 64, NOSTREAM) == -8
+
+
+def test_auto_split_and_validation():
+    lib = _lib()
+    assert lib.mla_attn_auto_split(16384, 2048) == 8192
+    assert lib.mla_attn_auto_split(4096, 2048) == 4096          # every row head-major
+    assert lib.mla_attn_auto_split(1100, 100) == 256
+    assert lib.mla_attn_auto_split(300, 40) == 0                # every row in the latent form
+    assert lib.mla_attn_auto_split(0, 16) == -1
+    assert lib.mla_attn_auto_workspace_bytes(0, 64, 16) == 0
+    # all head-major: per-head keys/values and bitmap of both sequences, no latent part
+    ws = lib.mla_attn_auto_workspace_bytes(2, 4096, 2048)
+    assert ws == 2 * (128 * 4096 * 256 * 2 + 128 * 4096 * 4)
+    GB = 1 << 30
+    Q, CKV, KPE, W, TK, OUT, WS = (GB * i for i in range(1, 8))
+    wsb = lib.mla_attn_auto_workspace_bytes(1, 1100, 100)
+
+    def call(q=Q, out=OUT, wk=WS, wsb=wsb, T=1100, scale=0.135):
+        return lib.mla_sparse_prefill_attn_auto(q, CKV, KPE, W, TK, 1, T, 100, scale, out, wk, wsb, NOSTREAM)
+    assert call(q=None) == -1
+    assert call(T=0) == -2
+    assert call(out=OUT + 2) == -3
+    assert call(wsb=wsb - 1) == -4
+    assert call(scale=float("nan")) == -7
+    assert call(out=Q) == -8

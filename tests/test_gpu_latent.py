@@ -184,3 +184,38 @@ def test_latent_workload_sampled(name):
         say(f"checking {len(rows)} sampled rows of batch {b}")
         ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], b, rows)
         attention_close(to_host(out[b, rows]), ref, f"{name} batch {b}")
+
+
+# ------------------------------------------------------------------------------------ split form
+# (1, 1100, 100): split 256 (rows 0-255 head-major, 256-1099 latent); (2, 700, 64): split 256 with
+# two sequences; (1, 300, 40): split 0 (all latent); (1, 200, 2048): split = T (all head-major).
+@pytest.mark.parametrize("B,T,K", [(1, 1100, 100), (2, 700, 64), (1, 300, 40), (1, 200, 2048)])
+def test_auto_attention_matches_oracle(B, T, K):
+    split = mla.mla_attn_auto_split(T, K)
+    say(f"split form B={B} T={T} K={K} split={split}")
+    q, c_kv, k_pe, w, topk = _latent_inputs(5300 + T + K, B, T, K)
+    out = mla.mla_sparse_prefill_attn_auto(to_dev(q), to_dev(c_kv), to_dev(k_pe), to_dev(w),
+                                           torch.from_numpy(topk).to(dev()), SCALE)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    _, ref = _oracle(q, c_kv, k_pe, w, topk)
+    attention_close(got, ref, f"split form B{B} T{T} K{K}")
+
+
+def test_auto_long_workload_sampled():
+    w = synth.WORKLOADS["long"]
+    d = synth.make(w)
+    x, wd, wu, q = to_dev(d["x"]), to_dev(d["w_dkv"]), to_dev(d["w_ukv"]), to_dev(d["q"])
+    gain = torch.from_numpy(d["gain"]).to(dev())
+    topk = torch.from_numpy(d["topk"]).to(dev())
+    _, c_kv, k_pe = mla.mla_kv_latent(x, wd, gain, 1e-6)
+    out = mla.mla_sparse_prefill_attn_auto(q, c_kv, k_pe, wu, topk, SCALE)
+    torch.cuda.synchronize()
+    split = mla.mla_attn_auto_split(w.T, w.K)
+    assert 0 < split < w.T
+    ckv_bits = c_kv.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    kpe_bits = k_pe.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    rows = [0, 1, split - 256, split - 1, split, split + 1, w.T - 1]
+    say(f"split {split}: checking rows {rows}")
+    ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], 0, rows)
+    attention_close(to_host(out[0, rows]), ref, "long split form")
