@@ -126,6 +126,7 @@ struct Stage {
     uint16_t* kp;
     uint16_t* v;
     uint32_t* bm;
+    uint32_t kn_l, kp_l, v_l, bm_l;   // the same as 32-bit LDS addresses (load destinations)
 };
 
 __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -208,7 +209,12 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     __shared__ __attribute__((aligned(16))) uint16_t kpA[kKT * 64], kpB[kKT * 64], kpC[kKT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t vA[kKT * 128], vB[kKT * 128], vC[kKT * 128];
     __shared__ __attribute__((aligned(16))) uint32_t bmA[2 * kQT], bmB[2 * kQT], bmC[2 * kQT];
-    const Stage stA{knA, kpA, vA, bmA}, stB{knB, kpB, vB, bmB}, stC{knC, kpC, vC, bmC};
+    // each thread's fixed load offsets (four key/value rows, one rotary row), kept in LDS rather
+    // than in registers: they are read once per tile
+    __shared__ __attribute__((aligned(16))) uint32_t off_lds[kWaves * 64 * 5];
+    const Stage stA{knA, kpA, vA, bmA, lds_addr(knA), lds_addr(kpA), lds_addr(vA), lds_addr(bmA)};
+    const Stage stB{knB, kpB, vB, bmB, lds_addr(knB), lds_addr(kpB), lds_addr(vB), lds_addr(bmB)};
+    const Stage stC{knC, kpC, vC, bmC, lds_addr(knC), lds_addr(kpC), lds_addr(vC), lds_addr(bmC)};
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,20 +274,28 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
         src_off[k] = (uint32_t)(row * 512 + lc * 16 + (kn_wave ? 0 : 2 * kNope));
     }
     const int kp_row = 8 * wave + (lane >> 3);
-    const uint32_t kp_off = (uint32_t)(kp_row * 2 * kRope + (((lane & 7) ^ ((kp_row >> 1) & 7)) << 4));
+    {
+        const uint32_t kp_off0 = (uint32_t)(kp_row * 2 * kRope + (((lane & 7) ^ ((kp_row >> 1) & 7)) << 4));
+        *reinterpret_cast<u32x4*>(off_lds + 4 * tid) = u32x4{src_off[0], src_off[1], src_off[2], src_off[3]};
+        off_lds[kWaves * 64 * 4 + tid] = kp_off0;
+    }
     auto issue_tile = [&](const Stage& st, int kt) {
+        const u32x4 src_o = *reinterpret_cast<const u32x4*>(off_lds + 4 * tid);
+        const uint32_t kp_off = off_lds[kWaves * 64 * 4 + tid];
         const int t0 = kt * kKT;
-        uint16_t* dst = kn_wave ? st.kn : st.v;
+        const uint32_t dst = kn_wave ? st.kn_l : st.v_l;
         const int tl = T - 1 - t0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int row = 16 * (wave & 3) + 4 * k + r16;
             const int dr = min(row, tl) - row;
-            dma16(kvh + (size_t)t0 * 256, src_off[k] + (uint32_t)(dr * 512), dst + (16 * (wave & 3) + 4 * k) * 128);
+            dma16_lds(kvh + (size_t)t0 * 256, src_o[k] + (uint32_t)(dr * 512),
+                      dst + (uint32_t)((16 * (wave & 3) + 4 * k) * 128 * 2));
         }
         const int drp = min(kp_row, tl) - kp_row;
-        dma16(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp + 8 * wave * 64);
-        if (wave < 2) dma16(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm + wave * kQT);
+        dma16_lds(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp_l + (uint32_t)(8 * wave * 64 * 2));
+        if (wave < 2)
+            dma16_lds(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm_l + (uint32_t)(wave * kQT * 4));
     };
 
     // ---- per-lane LDS read offsets (bytes).
@@ -308,17 +322,23 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     auto s_tile = [&](const Stage& st, f32x16 s[2]) {
         const uint8_t* kn = reinterpret_cast<const uint8_t*>(st.kn);
         const uint8_t* kp = reinterpret_cast<const uint8_t*>(st.kp);
+        auto rd = [&](int j, int blk) -> bf16x8 {
+            return j < 8 ? as_bf16x8(lds_read16(kn + blk * 32 * 256 + kn_off[j]))
+                         : as_bf16x8(lds_read16(kp + blk * 32 * 128 + kpr_off[j - 8]));
+        };
         s[0] = f32x16{};
         s[1] = f32x16{};
+        // the 24 key operands (step j, block b) in order 2j + b, each read three MFMAs ahead
+        bf16x8 r0 = rd(0, 0), r1 = rd(0, 1), r2 = rd(1, 0);
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
-            s[0] = mfma32x32x16(as_bf16x8(lds_read16(kn + kn_off[kc])), qf[kc], s[0]);
-            s[1] = mfma32x32x16(as_bf16x8(lds_read16(kn + 32 * 256 + kn_off[kc])), qf[kc], s[1]);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            s[0] = mfma32x32x16(as_bf16x8(lds_read16(kp + kpr_off[kc])), qf[8 + kc], s[0]);
-            s[1] = mfma32x32x16(as_bf16x8(lds_read16(kp + 32 * 128 + kpr_off[kc])), qf[8 + kc], s[1]);
+        for (int i = 0; i < 24; ++i) {
+            const int j = i >> 1, blk = i & 1;
+            bf16x8 nx;
+            if (i + 3 < 24) nx = rd((i + 3) >> 1, (i + 3) & 1);
+            s[blk] = mfma32x32x16(r0, qf[j], s[blk]);
+            r0 = r1;
+            r1 = r2;
+            r2 = nx;
         }
     };
     auto pv_tile = [&](const Stage& st, const bf16x8 pf[2][2]) {

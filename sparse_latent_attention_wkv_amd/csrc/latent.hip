@@ -318,14 +318,6 @@ __device__ __forceinline__ void mfma_vgpr(f32x16& c, const bf16x8& a, const bf16
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16& c0, f32x16& c1) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
 }
-// Direct global->LDS load with the LDS address given as a 32-bit LDS byte address (wave-uniform):
-// lane l's 16 bytes at sbase + voff land at lds + 16 l (as dma16).
-__device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
-}
 __device__ __forceinline__ constexpr int lat_sigma(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 // Queries s_lo..T-1 of every sequence; query row r = b*(T - s_lo) + s - s_lo indexes the

@@ -76,6 +76,19 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, void* ld
                  : "v"(voff), "s"(uniform_ptr(sbase)), "s"(l)
                  : "memory", "m0");
 }
+// The same load with the LDS destination given as a 32-bit LDS byte address (wave-uniform), so
+// no generic-to-LDS pointer conversion (and its null check) is needed per load.
+__device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(uniform32(lds))
+                 : "memory", "m0");
+}
+// 32-bit LDS byte address of an LDS object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) T*)p;
+}
 // s_waitcnt immediate for vmcnt(n), n < 64 (bits 3:0 and 15:14), other counters unconstrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // Workgroup barrier without the release fence of __syncthreads(), whose vmcnt(0) would drain
