@@ -494,31 +494,11 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
         for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
         return lane_pair_max(mx) * c2;
     };
-    auto softmax_tile = [&](const f32x16& sc, bf16x8 pf[2]) __attribute__((always_inline)) {
-        const float mt = tile_max(sc);
-        if (m_ref == -INFINITY) m_ref = mt;    // first tile: it holds a selected key
-        bad = bad || mt > m_ref + 64.0f;
-        const float nb = -m_ref;
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 pk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[8 * c + 2 * i], c2, nb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[8 * c + 2 * i + 1], c2, nb));
-                pk[i] = pack_bf16(p0, p1);
-                acc0 += p0;
-                acc1 += p1;
-            }
-            pf[c] = as_bf16x8(pk);
-        }
-        l_run += acc0 + acc1;
-    };
-    // The same softmax split into 14 pieces of a few vector instructions, one per score step of
-    // the next tile, so it runs while the matrix core works: pieces 0-3 the max over the lane's
-    // 16 scores, 4 the exchange with lane l ^ 32 and the reference, 5-12 two exponentials each,
-    // 13 the row sum. sv: the tile's masked scores; the probabilities land in pf.
+    // The softmax of one tile, split into 14 pieces of a few vector instructions, one per score
+    // step of the next tile, so it runs while the matrix core works: pieces 0-3 the max over
+    // the lane's 16 scores, 4 the exchange with lane l ^ 32 and the reference, 5-12 two
+    // exponentials each, 13 the row sum. sv: the tile's masked scores; the probabilities land
+    // in pf.
     f32x16 sv;
     bf16x8 pf[2];
     float smx = 0.f, snb = 0.f, sacc0 = 0.f, sacc1 = 0.f;
