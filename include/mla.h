@@ -16,6 +16,11 @@
  *                            the top-k selection intersected with the causal mask, softmax over
  *                            keys, value mixing ("DeepSeek-V3.2-Exp · Keys": MHA-prefill code
  *                            excerpt; "DeepSeek-V3.2-Exp · Scale scores": formula).
+ *   mla_kv_latent_cache      mla_kv_latent plus the FP8 round trip of the latent and the
+ *                            latent / rotary-key cache writes (the down-projection page's
+ *                            KV-cache evidence).
+ *   mla_window_kv            V4.1 window keys/values: norm, rotary tail, FP8 round trip, ring
+ *                            buffer ("DeepSeek V4.1 · Key-value RMSNorm": window-KV excerpt).
  *
  * Conventions for every call
  *  - Pointers marked (device) are HIP device pointers; all tensors are dense, row-major,
@@ -113,6 +118,74 @@ int mla_kv_norm_rope(const void* kv_raw, int rows, int row_stride, int has_rope,
  *         MLA_E_LAUNCH.
  */
 int mla_rope_table(int T, float theta, float* rope_cs, void* stream);
+
+/*
+ * Latent front end with the FP8 round trip of the latent and the key-value cache writes
+ * ("DeepSeek-V3.2-Exp · Key-value down-projection": the MLA key-value excerpt, then the
+ * KV-cache evidence: the normalised latent is quantised to fp8 in blocks of 128 features and
+ * brought back — fp8 values times the block scale in float, cast to bf16 — and stored with the
+ * rotated key in two caches at positions start_pos..start_pos+T-1; the up-projection consumes
+ * the rounded latent). The quantiser is not on the pages; this library's: e4m3 (largest value
+ * 448), scale s = amax/448 in fp32 (scale_fmt 0) or that rounded up to a power of two
+ * (scale_fmt 1), code = e4m3 value nearest to x/s (correctly rounded fp32 division, ties to the
+ * even code), result bf16(code * s); a block of zeros stays zero.
+ *   x, w_dkv, kv_gain, eps  as for mla_kv_latent.
+ *   rope_cs     (device) fp32 [start_pos + T, 32, 2]: the table of mla_rope_table, indexed by
+ *               absolute position (row t of the call is position start_pos + t).
+ *   start_pos   first position of the call, >= 0.
+ *   kv_raw      (device, out) bf16 [B, T, 576]: the down-projection output.
+ *   c_kv        (device, out) bf16 [B, T, 512]: the rounded latent (input of mla_kv_up).
+ *   k_pe        (device, out) bf16 [B, T, 64]: the rotated key.
+ *   kv_cache    (device, in/out) bf16 [cache_batch, cache_len, 512]; rows [b, start_pos + t]
+ *               for b < B, t < T receive c_kv[b, t]; every other row is left as it was.
+ *   pe_cache    (device, in/out) bf16 [cache_batch, cache_len, 64]; the same rows receive k_pe.
+ *   cache_batch >= B;  cache_len >= start_pos + T.
+ *   c_norm      (device, out, may be NULL) bf16 [B, T, 512]: the normalised latent before the
+ *               round trip.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (B, T < 1, B*T > MLA_MAX_ROWS, start_pos < 0, the cache too
+ *         small, start_pos + T > MLA_MAX_ROWS), MLA_E_ALIGN, MLA_E_ARG (eps, or scale_fmt not 0
+ *         or 1), MLA_E_ALIAS, MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_kv_latent_cache(const void* x, const void* w_dkv, const float* kv_gain, float eps,
+                        const float* rope_cs, int B, int T, int start_pos, int scale_fmt,
+                        void* kv_raw, void* c_kv, void* k_pe, void* kv_cache, void* pe_cache,
+                        int cache_batch, int cache_len, void* c_norm, void* stream);
+
+/*
+ * The norm/rotary/round-trip/cache step alone (the second half of mla_kv_latent_cache), from a
+ * down-projection output kv_raw (device) bf16 [B, T, 576]. Other arguments and errors as for
+ * mla_kv_latent_cache.
+ */
+int mla_kv_norm_rope_cache(const void* kv_raw, int B, int T, int start_pos, const float* gain,
+                           float eps, const float* rope_cs, int scale_fmt, void* c_kv, void* k_pe,
+                           void* kv_cache, void* pe_cache, int cache_batch, int cache_len,
+                           void* c_norm, void* stream);
+
+/*
+ * V4.1 window keys/values ("DeepSeek V4.1 · Key-value RMSNorm", formula and window-KV excerpt):
+ * RMSNorm of the 512-wide projection output (the page's eps is 1e-20), rotary on its last 64
+ * features in place (pairs (2i, 2i+1) of the tail as complex numbers, angle
+ * position * theta^(-2i/64)), the FP8 round trip of mla_kv_latent_cache over the whole vector
+ * (rotary tail included), then the ring-buffer writes: position p = start_pos + s goes to slot
+ * p mod window, for the last min(S, window) positions of the call (the page's prefill branch
+ * at start_pos 0 and its one-position decode branch both write exactly these).
+ *   kv_raw        (device) bf16 [B, S, 512].
+ *   gain, eps     (device) fp32 [512]; eps finite and > 0 (host).
+ *   rope_cs       (device) fp32 [start_pos + S, 32, 2], by absolute position.
+ *   scale_fmt     0 or 1, as for mla_kv_latent_cache.
+ *   window        ring size, >= 1.
+ *   kv_out        (device, out) bf16 [B, S, 512]: the rounded vectors (the page's window_kv in
+ *                 prefill).
+ *   window_cache  (device, in/out) bf16 [cache_batch, window, 512]; slots not written keep
+ *                 their contents.
+ *   kv_pre        (device, out, may be NULL) bf16 [B, S, 512]: the vectors before the round trip.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (B, S, window < 1, B*S > MLA_MAX_ROWS, start_pos < 0,
+ *         cache_batch < B, start_pos + S > MLA_MAX_ROWS), MLA_E_ALIGN, MLA_E_ARG, MLA_E_ALIAS,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_window_kv(const void* kv_raw, int B, int S, int start_pos, const float* gain, float eps,
+                  const float* rope_cs, int scale_fmt, int window, void* kv_out,
+                  void* window_cache, int cache_batch, void* kv_pre, void* stream);
 
 /*
  * KV up-projection into head-major keys and values.

@@ -160,8 +160,7 @@ def window_kv(kv_raw, gain, window_cache, start_pos: int = 0, eps: float = RMS_E
     updated ring buffer."""
     kv_raw = np.asarray(kv_raw, np.float32)
     B, S, D = kv_raw.shape
-    cache = np.array(window_cache, np.float32, copy=True)
-    W = cache.shape[1]
+    cache = np.asarray(window_cache, np.float32)
     if cache.shape[0] < B or cache.shape[2] != D:
         raise ValueError("window cache shape does not fit")
     y = rms_norm(kv_raw, gain, eps)
@@ -169,6 +168,17 @@ def window_kv(kv_raw, gain, window_cache, start_pos: int = 0, eps: float = RMS_E
     pre = y.copy()
     pre[..., D - rope_dim:] = tail
     kv = fp8_round_trip(pre, scale_fmt)
+    return pre, kv, ring_write(kv, cache, start_pos)
+
+
+def ring_write(kv, window_cache, start_pos: int):
+    """The window-KV excerpt's two ring-buffer branches on a copy of window_cache [Bc, W, D]:
+    prefill (start_pos 0) stores all S positions if S <= W, else the last W split at S mod W;
+    decode stores its one position at slot start_pos mod W."""
+    kv = np.asarray(kv, np.float32)
+    cache = np.array(window_cache, np.float32, copy=True)
+    B, S, _ = kv.shape
+    W = cache.shape[1]
     if start_pos == 0:
         if S <= W:
             cache[:B, :S] = kv
@@ -181,4 +191,4 @@ def window_kv(kv_raw, gain, window_cache, start_pos: int = 0, eps: float = RMS_E
         if S != 1:
             raise ValueError("the decode branch writes one position")
         cache[:B, start_pos % W] = kv[:, 0]
-    return pre, kv, cache
+    return cache

@@ -27,6 +27,11 @@ _SIGS = {
     "mla_kv_latent": (_I, [_VP, _VP, _VP, _F, _VP, _I, _I, _VP, _VP, _VP, _VP]),
     "mla_kv_norm_rope": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _VP, _VP, _VP]),
     "mla_rope_table": (_I, [_I, _F, _VP, _VP]),
+    "mla_kv_latent_cache": (_I, [_VP, _VP, _VP, _F, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP,
+                                 _I, _I, _VP, _VP]),
+    "mla_kv_norm_rope_cache": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _VP, _VP, _VP, _VP, _I, _I,
+                                    _VP, _VP]),
+    "mla_window_kv": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "mla_kv_up": (_I, [_VP, _VP, _I, _I, _VP, _VP]),
     "mla_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
     "mla_selection_bitmap": (_I, [_VP, _I, _I, _I, _VP, _VP]),
@@ -161,6 +166,120 @@ def mla_kv_norm_rope(kv_raw, gain, eps: float = 1e-6, rope_cs=None, T: int | Non
                                       _ptr(rope_cs), T or 1, _ptr(c_kv), _ptr(k_pe),
                                       _stream(kv_raw.device)))
     return c_kv, k_pe
+
+
+def _positions_table(rope_cs, start_pos: int, n: int, device):
+    if rope_cs is None:
+        return mla_rope_table(start_pos + n, device)
+    _need(rope_cs, "rope_cs", torch.float32)
+    if rope_cs.dim() != 3 or rope_cs.shape[1:] != (32, 2) or rope_cs.shape[0] < start_pos + n:
+        raise ValueError(f"rope_cs must be [>= {start_pos + n}, 32, 2] fp32")
+    return rope_cs
+
+
+def _cache_pair(kv_cache, pe_cache, B: int, T: int, start_pos: int):
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(pe_cache, "pe_cache", torch.bfloat16)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != KV_LORA:
+        raise ValueError("kv_cache must be [cache_batch, cache_len, 512]")
+    cb, cl, _ = kv_cache.shape
+    if tuple(pe_cache.shape) != (cb, cl, ROPE):
+        raise ValueError("pe_cache must be [cache_batch, cache_len, 64] like kv_cache")
+    if cb < B or cl < start_pos + T:
+        raise ValueError("caches too small for these batch rows and positions")
+    return cb, cl
+
+
+def mla_kv_latent_cache(x, w_dkv, kv_gain, kv_cache, pe_cache, start_pos: int = 0,
+                        eps: float = 1e-6, scale_fmt: int = 0, rope_cs=None,
+                        want_norm: bool = False):
+    """x [B, T, 7168] bf16 at positions start_pos.. -> (kv_raw [B, T, 576], c_kv [B, T, 512]
+    rounded through fp8, k_pe [B, T, 64]) bf16, plus c_norm (before the round trip) when
+    ``want_norm``; rows start_pos.. of kv_cache [Bc, L, 512] / pe_cache [Bc, L, 64] are
+    written in place. scale_fmt 0: fp32 block scale, 1: power-of-two block scale."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, 7168]")
+    B, T, _ = x.shape
+    _need(x, "x", torch.bfloat16, (B, T, HIDDEN))
+    _need(w_dkv, "w_dkv", torch.bfloat16, (KV_A_OUT, HIDDEN))
+    _need(kv_gain, "kv_gain", torch.float32, (KV_LORA,))
+    cb, cl = _cache_pair(kv_cache, pe_cache, B, T, start_pos)
+    rope_cs = _positions_table(rope_cs, start_pos, T, x.device)
+    dev = x.device
+    kv_raw = torch.empty((B, T, KV_A_OUT), dtype=torch.bfloat16, device=dev)
+    c_kv = torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=dev)
+    k_pe = torch.empty((B, T, ROPE), dtype=torch.bfloat16, device=dev)
+    c_norm = torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=dev) if want_norm else None
+    with torch.cuda.device(dev):
+        _check(lib().mla_kv_latent_cache(_ptr(x), _ptr(w_dkv), _ptr(kv_gain), eps, _ptr(rope_cs),
+                                         B, T, start_pos, scale_fmt, _ptr(kv_raw), _ptr(c_kv),
+                                         _ptr(k_pe), _ptr(kv_cache), _ptr(pe_cache), cb, cl,
+                                         _ptr(c_norm), _stream(dev)))
+    return (kv_raw, c_kv, k_pe, c_norm) if want_norm else (kv_raw, c_kv, k_pe)
+
+
+def mla_kv_norm_rope_cache(kv_raw, gain, kv_cache, pe_cache, start_pos: int = 0,
+                           eps: float = 1e-6, scale_fmt: int = 0, rope_cs=None,
+                           want_norm: bool = False, out=None):
+    """The norm / rotary / fp8 round trip / cache step of mla_kv_latent_cache from
+    kv_raw [B, T, 576] bf16 -> (c_kv, k_pe[, c_norm]). `out` = (c_kv, k_pe[, c_norm]) reuses
+    caller buffers."""
+    if kv_raw.dim() != 3:
+        raise ValueError("kv_raw must be [B, T, 576]")
+    B, T, _ = kv_raw.shape
+    _need(kv_raw, "kv_raw", torch.bfloat16, (B, T, KV_A_OUT))
+    _need(gain, "gain", torch.float32, (KV_LORA,))
+    cb, cl = _cache_pair(kv_cache, pe_cache, B, T, start_pos)
+    rope_cs = _positions_table(rope_cs, start_pos, T, kv_raw.device)
+    dev = kv_raw.device
+    if out is None:
+        out = (torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, ROPE), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=dev) if want_norm else None)
+    c_kv, k_pe = out[0], out[1]
+    c_norm = out[2] if len(out) > 2 else None
+    _need(c_kv, "c_kv", torch.bfloat16, (B, T, KV_LORA))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
+    if c_norm is not None:
+        _need(c_norm, "c_norm", torch.bfloat16, (B, T, KV_LORA))
+    with torch.cuda.device(dev):
+        _check(lib().mla_kv_norm_rope_cache(_ptr(kv_raw), B, T, start_pos, _ptr(gain), eps,
+                                            _ptr(rope_cs), scale_fmt, _ptr(c_kv), _ptr(k_pe),
+                                            _ptr(kv_cache), _ptr(pe_cache), cb, cl, _ptr(c_norm),
+                                            _stream(dev)))
+    return (c_kv, k_pe, c_norm) if c_norm is not None else (c_kv, k_pe)
+
+
+def mla_window_kv(kv_raw, gain, window_cache, start_pos: int = 0, eps: float = 1e-20,
+                  scale_fmt: int = 0, rope_cs=None, want_pre: bool = False, out=None):
+    """V4.1 window keys/values: kv_raw [B, S, 512] bf16 -> kv [B, S, 512] (norm, rotary tail,
+    fp8 round trip), plus kv_pre (before the round trip) when ``want_pre``; the last
+    min(S, window) positions go to slot position % window of window_cache [Bc, window, 512]
+    in place. `out` = (kv[, kv_pre]) reuses caller buffers."""
+    if kv_raw.dim() != 3:
+        raise ValueError("kv_raw must be [B, S, 512]")
+    B, S, _ = kv_raw.shape
+    _need(kv_raw, "kv_raw", torch.bfloat16, (B, S, KV_LORA))
+    _need(gain, "gain", torch.float32, (KV_LORA,))
+    _need(window_cache, "window_cache", torch.bfloat16)
+    if window_cache.dim() != 3 or window_cache.shape[2] != KV_LORA or window_cache.shape[0] < B:
+        raise ValueError("window_cache must be [cache_batch >= B, window, 512]")
+    cb, W, _ = window_cache.shape
+    rope_cs = _positions_table(rope_cs, start_pos, S, kv_raw.device)
+    dev = kv_raw.device
+    if out is None:
+        out = (torch.empty((B, S, KV_LORA), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, S, KV_LORA), dtype=torch.bfloat16, device=dev) if want_pre else None)
+    kv = out[0]
+    pre = out[1] if len(out) > 1 else None
+    _need(kv, "kv", torch.bfloat16, (B, S, KV_LORA))
+    if pre is not None:
+        _need(pre, "kv_pre", torch.bfloat16, (B, S, KV_LORA))
+    with torch.cuda.device(dev):
+        _check(lib().mla_window_kv(_ptr(kv_raw), B, S, start_pos, _ptr(gain), eps, _ptr(rope_cs),
+                                   scale_fmt, W, _ptr(kv), _ptr(window_cache), cb, _ptr(pre),
+                                   _stream(dev)))
+    return (kv, pre) if pre is not None else kv
 
 
 def mla_kv_up(c_kv, w_ukv, out=None):

@@ -94,6 +94,46 @@ int validate_norm_rope(const void* kv_raw, int rows, int row_stride, int has_rop
     return MLA_OK;
 }
 
+// Checks shared by the cached front end and the window form: B*T rows at positions
+// start_pos..start_pos+T-1, the rotary table covering them, the scale format.
+int validate_positions(int B, int T, int start_pos, int scale_fmt, float eps) {
+    if (B < 1 || T < 1 || (size_t)B * T > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (start_pos < 0 || (int64_t)start_pos + T > (int64_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!pos_finite(eps) || (scale_fmt != 0 && scale_fmt != 1)) return MLA_E_ARG;
+    return MLA_OK;
+}
+
+int validate_norm_rope_cache(const void* kv_raw, int B, int T, int start_pos, const float* gain,
+                             float eps, const float* rope_cs, int scale_fmt, const void* c_kv,
+                             const void* k_pe, const void* kv_cache, const void* pe_cache,
+                             int cache_batch, int cache_len, const void* c_norm,
+                             bool kv_raw_is_output) {
+    if (!kv_raw || !gain || !rope_cs || !c_kv || !k_pe || !kv_cache || !pe_cache) return MLA_E_NULL;
+    int st = validate_positions(B, T, start_pos, scale_fmt, eps);
+    if (st != MLA_OK) return st;
+    if (cache_batch < B || cache_len < 1 || (int64_t)start_pos + T > cache_len) return MLA_E_SHAPE;
+    if (!aligned16(kv_raw) || !aligned16(gain) || !aligned16(rope_cs) || !aligned16(c_kv) ||
+        !aligned16(k_pe) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+        (c_norm && !aligned16(c_norm)))
+        return MLA_E_ALIGN;
+    const size_t M = (size_t)B * T;
+    const Span raw = {kv_raw, M * MLA_KV_A_OUT * kBf16};
+    const Span ins[] = {raw,
+                        {gain, MLA_KV_LORA * sizeof(float)},
+                        {rope_cs, (size_t)(start_pos + T) * 64 * sizeof(float)}};
+    const Span outs[] = {{c_kv, M * MLA_KV_LORA * kBf16},
+                         {k_pe, M * MLA_ROPE * kBf16},
+                         {kv_cache, (size_t)cache_batch * cache_len * MLA_KV_LORA * kBf16},
+                         {pe_cache, (size_t)cache_batch * cache_len * MLA_ROPE * kBf16},
+                         {c_norm, c_norm ? M * MLA_KV_LORA * kBf16 : 0},
+                         {kv_raw_is_output ? kv_raw : nullptr, kv_raw_is_output ? raw.bytes : 0}};
+    // kv_raw is an input of the norm step; when the call also produces it, it counts as an
+    // output (checked against every other buffer) instead.
+    if (any_alias(outs, 6, kv_raw_is_output ? ins + 1 : ins, kv_raw_is_output ? 2 : 3))
+        return MLA_E_ALIAS;
+    return MLA_OK;
+}
+
 int validate_topk(const int32_t* topk, int B, int T, int K) {
     if (!topk) return MLA_E_NULL;
     if (B < 1 || T < 1 || K < 1 || T > MLA_MAX_T || K > 65536) return MLA_E_SHAPE;
@@ -152,6 +192,81 @@ int mla_kv_latent(const void* x, const void* w_dkv, const float* kv_gain, float 
     return launched(mla::launch_norm_rope(static_cast<const uint16_t*>(kv_raw), (int)M, MLA_KV_A_OUT,
                                           true, kv_gain, eps, rope_cs, T, static_cast<uint16_t*>(c_kv),
                                           static_cast<uint16_t*>(k_pe), s));
+}
+
+int mla_kv_norm_rope_cache(const void* kv_raw, int B, int T, int start_pos, const float* gain,
+                           float eps, const float* rope_cs, int scale_fmt, void* c_kv, void* k_pe,
+                           void* kv_cache, void* pe_cache, int cache_batch, int cache_len,
+                           void* c_norm, void* stream) {
+    int st = validate_norm_rope_cache(kv_raw, B, T, start_pos, gain, eps, rope_cs, scale_fmt, c_kv,
+                                      k_pe, kv_cache, pe_cache, cache_batch, cache_len, c_norm,
+                                      false);
+    if (st != MLA_OK) return st;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_kv_norm_rope_cache(
+        static_cast<const uint16_t*>(kv_raw), B, T, start_pos, gain, eps, rope_cs, scale_fmt,
+        static_cast<uint16_t*>(c_kv), static_cast<uint16_t*>(c_norm), static_cast<uint16_t*>(k_pe),
+        static_cast<uint16_t*>(kv_cache), static_cast<uint16_t*>(pe_cache), cache_len,
+        static_cast<hipStream_t>(stream)));
+}
+
+int mla_kv_latent_cache(const void* x, const void* w_dkv, const float* kv_gain, float eps,
+                        const float* rope_cs, int B, int T, int start_pos, int scale_fmt,
+                        void* kv_raw, void* c_kv, void* k_pe, void* kv_cache, void* pe_cache,
+                        int cache_batch, int cache_len, void* c_norm, void* stream) {
+    if (!x || !w_dkv) return MLA_E_NULL;
+    int st = validate_norm_rope_cache(kv_raw, B, T, start_pos, kv_gain, eps, rope_cs, scale_fmt,
+                                      c_kv, k_pe, kv_cache, pe_cache, cache_batch, cache_len,
+                                      c_norm, true);
+    if (st != MLA_OK) return st;
+    if (!aligned16(x) || !aligned16(w_dkv)) return MLA_E_ALIGN;
+    const size_t M = (size_t)B * T;
+    // The weights and activations must not overlap any output either.
+    const Span ins[] = {{x, M * MLA_HIDDEN * kBf16},
+                        {w_dkv, (size_t)MLA_KV_A_OUT * MLA_HIDDEN * kBf16}};
+    const Span outs[] = {{kv_raw, M * MLA_KV_A_OUT * kBf16},
+                         {c_kv, M * MLA_KV_LORA * kBf16},
+                         {k_pe, M * MLA_ROPE * kBf16},
+                         {kv_cache, (size_t)cache_batch * cache_len * MLA_KV_LORA * kBf16},
+                         {pe_cache, (size_t)cache_batch * cache_len * MLA_ROPE * kBf16},
+                         {c_norm, c_norm ? M * MLA_KV_LORA * kBf16 : 0}};
+    if (any_alias(outs, 6, ins, 2)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(mla::launch_gemm_kv_down(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(w_dkv), (int)M,
+                                           static_cast<uint16_t*>(kv_raw), s));
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_kv_norm_rope_cache(
+        static_cast<const uint16_t*>(kv_raw), B, T, start_pos, kv_gain, eps, rope_cs, scale_fmt,
+        static_cast<uint16_t*>(c_kv), static_cast<uint16_t*>(c_norm), static_cast<uint16_t*>(k_pe),
+        static_cast<uint16_t*>(kv_cache), static_cast<uint16_t*>(pe_cache), cache_len, s));
+}
+
+int mla_window_kv(const void* kv_raw, int B, int S, int start_pos, const float* gain, float eps,
+                  const float* rope_cs, int scale_fmt, int window, void* kv_out,
+                  void* window_cache, int cache_batch, void* kv_pre, void* stream) {
+    if (!kv_raw || !gain || !rope_cs || !kv_out || !window_cache) return MLA_E_NULL;
+    int st = validate_positions(B, S, start_pos, scale_fmt, eps);
+    if (st != MLA_OK) return st;
+    if (window < 1 || cache_batch < B) return MLA_E_SHAPE;
+    if ((size_t)cache_batch * window > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(kv_raw) || !aligned16(gain) || !aligned16(rope_cs) || !aligned16(kv_out) ||
+        !aligned16(window_cache) || (kv_pre && !aligned16(kv_pre)))
+        return MLA_E_ALIGN;
+    const size_t M = (size_t)B * S;
+    const Span ins[] = {{kv_raw, M * MLA_KV_LORA * kBf16},
+                        {gain, MLA_KV_LORA * sizeof(float)},
+                        {rope_cs, (size_t)(start_pos + S) * 64 * sizeof(float)}};
+    const Span outs[] = {{kv_out, M * MLA_KV_LORA * kBf16},
+                         {window_cache, (size_t)cache_batch * window * MLA_KV_LORA * kBf16},
+                         {kv_pre, kv_pre ? M * MLA_KV_LORA * kBf16 : 0}};
+    if (any_alias(outs, 3, ins, 3)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_window_kv(
+        static_cast<const uint16_t*>(kv_raw), B, S, start_pos, gain, eps, rope_cs, scale_fmt, window,
+        static_cast<uint16_t*>(kv_out), static_cast<uint16_t*>(kv_pre),
+        static_cast<uint16_t*>(window_cache), static_cast<hipStream_t>(stream)));
 }
 
 int mla_rope_table(int T, float theta, float* rope_cs, void* stream) {

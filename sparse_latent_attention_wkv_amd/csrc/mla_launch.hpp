@@ -11,6 +11,16 @@ hipError_t launch_norm_rope(const uint16_t* src, int rows, int stride, bool rope
                             float eps, const float* rope_cs, int T, uint16_t* c_kv, uint16_t* k_pe,
                             hipStream_t stream);
 hipError_t launch_rope_table(int T, double theta, float* rope_cs, hipStream_t stream);
+// Norm/rotary pass with the fp8 round trip of the latent and the cache writes (rows b*T + t at
+// position start_pos + t), and the window-KV form (ring buffer of `window` positions).
+hipError_t launch_kv_norm_rope_cache(const uint16_t* kv_raw, int B, int T, int start_pos,
+                                     const float* gain, float eps, const float* rope_cs,
+                                     int pow2_scale, uint16_t* c_kv, uint16_t* c_norm,
+                                     uint16_t* k_pe, uint16_t* kv_cache, uint16_t* pe_cache,
+                                     int cache_len, hipStream_t stream);
+hipError_t launch_window_kv(const uint16_t* kv_raw, int B, int S, int start_pos, const float* gain,
+                            float eps, const float* rope_cs, int pow2_scale, int window,
+                            uint16_t* out, uint16_t* pre, uint16_t* cache, hipStream_t stream);
 hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, uint16_t* kv_raw,
                                hipStream_t stream);
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,

@@ -193,3 +193,74 @@ def test_auto_split_and_validation():
     assert call(wsb=wsb - 1) == -4
     assert call(scale=float("nan")) == -7
     assert call(out=Q) == -8
+
+
+def test_kv_latent_cache_validation():
+    lib = _lib()
+    MB = 1 << 26                                       # 64 MiB apart: caches span a few MB
+    X, W, G_, CS, RAW, CKV, KPE, KC, PC, CN = (MB * i for i in range(1, 11))
+    ok = dict(x=X, w=W, g=G_, eps=1e-6, cs=CS, B=2, T=8, sp=4, fmt=0, raw=RAW, ckv=CKV, kpe=KPE,
+              kc=KC, pc=PC, cb=2, cl=16, cn=CN)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.mla_kv_latent_cache(a["x"], a["w"], a["g"], a["eps"], a["cs"], a["B"], a["T"],
+                                       a["sp"], a["fmt"], a["raw"], a["ckv"], a["kpe"], a["kc"],
+                                       a["pc"], a["cb"], a["cl"], a["cn"], NOSTREAM)
+
+    def norm_call(**kw):
+        a = {**ok, **kw}
+        return lib.mla_kv_norm_rope_cache(a["raw"], a["B"], a["T"], a["sp"], a["g"], a["eps"],
+                                          a["cs"], a["fmt"], a["ckv"], a["kpe"], a["kc"], a["pc"],
+                                          a["cb"], a["cl"], a["cn"], NOSTREAM)
+    for f in (call, norm_call):
+        assert f() == -5                               # valid: only the device check fails here
+        assert f(raw=None) == -1
+        assert f(kc=None) == -1
+        assert f(pc=None) == -1
+        assert f(B=0) == -2
+        assert f(sp=-1) == -2
+        assert f(cl=11) == -2                          # start_pos + T = 12 > cache_len
+        assert f(cb=1) == -2                           # cache_batch < B
+        assert f(kc=KC + 2) == -3
+        assert f(cn=CN + 8) == -3
+        assert f(fmt=2) == -7
+        assert f(eps=0.0) == -7
+        assert f(kc=CKV) == -8                         # cache overlapping the rounded latent
+        assert f(pc=KC + 1024) == -8                   # the two caches overlapping
+        assert f(cn=RAW) == -8
+        assert f(cs=KC) == -8                          # rotary table inside an output
+    assert call(x=None) == -1
+    assert call(w=W + 4) == -3
+    assert call(raw=X) == -8
+    assert call(kc=W) == -8
+    assert norm_call(ckv=RAW + 64) == -8               # output inside the input rows
+
+
+def test_window_kv_validation():
+    lib = _lib()
+    MB = 1 << 24
+    RAW, G_, CS, OUT, WC, PRE = (MB * i for i in range(1, 7))
+    ok = dict(raw=RAW, B=4, S=1, sp=100, g=G_, eps=1e-20, cs=CS, fmt=1, win=8, out=OUT, wc=WC,
+              cb=4, pre=PRE)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.mla_window_kv(a["raw"], a["B"], a["S"], a["sp"], a["g"], a["eps"], a["cs"],
+                                 a["fmt"], a["win"], a["out"], a["wc"], a["cb"], a["pre"], NOSTREAM)
+    assert call() == -5
+    assert call(pre=None) == -5
+    assert call(raw=None) == -1
+    assert call(wc=None) == -1
+    assert call(out=None) == -1
+    assert call(S=0) == -2
+    assert call(win=0) == -2
+    assert call(cb=3) == -2
+    assert call(sp=-5) == -2
+    assert call(sp=(1 << 24)) == -2                    # positions beyond MLA_MAX_ROWS
+    assert call(pre=PRE + 4) == -3
+    assert call(fmt=-1) == -7
+    assert call(eps=float("inf")) == -7
+    assert call(out=RAW) == -8
+    assert call(pre=OUT) == -8
+    assert call(wc=CS) == -8
