@@ -163,8 +163,29 @@ def side_measurements(torch, mla, dev, stream, topk, B: int, T: int, K: int) -> 
     w_bytes = 3072.0 * 256
     window = {"rows": 256, "us": us_w, "GB_s": w_bytes / (us_w * 1e-6) / 1e9, "bytes": w_bytes}
     del kv_raw, c_kv, k_pe, bm, kc, pc, wraw, wcache, wout
-    return {"norm_rope_frontend_B8_T4096": norm, "selection_bitmap": bitmap,
+    side = {"norm_rope_frontend_B8_T4096": norm, "selection_bitmap": bitmap,
             "norm_rope_fp8_cache_B8_T4096": cache, "window_kv_decode_B256": window}
+    side["query_path"] = query_path_measurement(torch, mla, dev, stream, B, T)
+    return side
+
+
+def query_path_measurement(torch, mla, dev, stream, B: int, T: int) -> dict:
+    """The query path (wq_a 7168 -> 1536, q_norm, wq_b 1536 -> 128 x 192 with the rotary part of
+    every head rotated) at the benchmarked batch and length, against the MFMA roofline:
+    2*M*1536*7168 + 2*M*24576*1536 FLOP for M = B*T tokens. Random weights of the layer's shapes."""
+    torch.manual_seed(1006)
+    M = B * T
+    x = torch.randn((B, T, 7168), device=dev).to(torch.bfloat16)
+    wa = (torch.randn((1536, 7168), device=dev) * 7168 ** -0.5).to(torch.bfloat16)
+    g = 1.0 + 0.1 ** 0.5 * torch.randn(1536, device=dev)
+    wb = (torch.randn((128 * 192, 1536), device=dev) * 1536 ** -0.5).to(torch.bfloat16)
+    cs = mla.mla_rope_table(T, dev)
+    out = mla.mla_q_path(x, wa, g, wb, rope_cs=cs)
+    us = timed_us(torch, stream, lambda: mla.mla_q_path(x, wa, g, wb, rope_cs=cs, out=out), reps=10, warm=3)
+    flop = 2.0 * M * 1536 * 7168 + 2.0 * M * 24576 * 1536
+    tf = flop / (us * 1e-6) / 1e12
+    del x, wa, wb, out
+    return {"tokens": M, "us": us, "TFLOP_s": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS, "flop": flop}
 
 
 def mfma_busy_record():

@@ -21,6 +21,8 @@
  *                            KV-cache evidence).
  *   mla_window_kv            V4.1 window keys/values: norm, rotary tail, FP8 round trip, ring
  *                            buffer ("DeepSeek V4.1 · Key-value RMSNorm": window-KV excerpt).
+ *   mla_q_path               the query path: wq_a, q_norm, wq_b, rotary of each head's rotary
+ *                            part (the MLA constructor excerpt's query modules).
  *
  * Conventions for every call
  *  - Pointers marked (device) are HIP device pointers; all tensors are dense, row-major,
@@ -57,6 +59,7 @@ extern "C" {
 #define MLA_QK_HEAD 192       /* MLA_QK_NOPE + MLA_ROPE */
 #define MLA_V_HEAD 128
 #define MLA_KV_B_OUT 32768    /* MLA_HEADS * (MLA_QK_NOPE + MLA_V_HEAD) */
+#define MLA_Q_LORA 1536       /* q_lora_rank: not on the pages; the library's fixed reading */
 #define MLA_MAX_T 32768       /* longest sequence the selection/attention calls accept */
 #define MLA_MAX_ROWS (1 << 24)
 
@@ -160,6 +163,31 @@ int mla_kv_norm_rope_cache(const void* kv_raw, int B, int T, int start_pos, cons
                            float eps, const float* rope_cs, int scale_fmt, void* c_kv, void* k_pe,
                            void* kv_cache, void* pe_cache, int cache_batch, int cache_len,
                            void* c_norm, void* stream);
+
+/*
+ * Query path ("DeepSeek-V3.2-Exp · Key-value down-projection": MLA constructor excerpt with wq_a,
+ * q_norm and wq_b; "DeepSeek-V3.2-Exp · Keys": MHA-prefill excerpt, q = [q_nope | q_pe] per head,
+ * and the indexer's qr argument). The forward is not on the pages; this library's reading:
+ * qa = bf16(x . W_qa^T), qr = bf16(q_gain * qa * rsqrt(mean(qa^2) + eps)) in fp32, q = bf16(qr .
+ * W_qb^T) viewed [B, T, 128, 192], and features 128..191 of every head (q_pe) rotated as the
+ * shared key is (pairs (2i, 2i+1) as complex numbers, angle (start_pos + t) * theta^(-2i/64),
+ * fp32 arithmetic on the bf16 values, rounded to bf16).
+ *   x          (device) bf16 [B, T, 7168].
+ *   w_qa       (device) bf16 [1536, 7168], [out, in].
+ *   q_gain     (device) fp32 [1536];  eps (host) finite and > 0 (the RMSNorm default is 1e-6).
+ *   w_qb       (device) bf16 [128 * 192, 1536], [out, in]; output feature h*192 + j is head h's
+ *              feature j (j < 128 non-rotary, j >= 128 rotary).
+ *   rope_cs    (device) fp32 [start_pos + T, 32, 2] (mla_rope_table), by absolute position.
+ *   q_rank     must be MLA_Q_LORA (1536).
+ *   qa         (device, out) bf16 [B, T, 1536]: the wq_a output.
+ *   qr         (device, out) bf16 [B, T, 1536]: the normalised low-rank query (the indexer's input).
+ *   q          (device, out) bf16 [B, T, 128, 192]: the query mla_sparse_prefill_attn takes.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (B, T < 1, B*T > MLA_MAX_ROWS, start_pos < 0, q_rank),
+ *         MLA_E_ALIGN, MLA_E_ARG (eps), MLA_E_ALIAS, MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_q_path(const void* x, const void* w_qa, const float* q_gain, float eps, const void* w_qb,
+               const float* rope_cs, int B, int T, int start_pos, int q_rank, void* qa, void* qr,
+               void* q, void* stream);
 
 /*
  * V4.1 window keys/values ("DeepSeek V4.1 · Key-value RMSNorm", formula and window-KV excerpt):

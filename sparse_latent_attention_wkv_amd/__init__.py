@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmla.so")
 
 HIDDEN, KV_LORA, ROPE, KV_A_OUT = 7168, 512, 64, 576
 HEADS, QK_NOPE, QK_HEAD, V_HEAD = 128, 128, 192, 128
+Q_LORA = 1536
 KV_B_OUT = HEADS * (QK_NOPE + V_HEAD)
 
 _lib = None
@@ -32,6 +33,7 @@ _SIGS = {
     "mla_kv_norm_rope_cache": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _VP, _VP, _VP, _VP, _I, _I,
                                     _VP, _VP]),
     "mla_window_kv": (_I, [_VP, _I, _I, _I, _VP, _F, _VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
+    "mla_q_path": (_I, [_VP, _VP, _VP, _F, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP]),
     "mla_kv_up": (_I, [_VP, _VP, _I, _I, _VP, _VP]),
     "mla_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
     "mla_selection_bitmap": (_I, [_VP, _I, _I, _I, _VP, _VP]),
@@ -280,6 +282,34 @@ def mla_window_kv(kv_raw, gain, window_cache, start_pos: int = 0, eps: float = 1
                                    scale_fmt, W, _ptr(kv), _ptr(window_cache), cb, _ptr(pre),
                                    _stream(dev)))
     return (kv, pre) if pre is not None else kv
+
+
+def mla_q_path(x, w_qa, q_gain, w_qb, start_pos: int = 0, eps: float = 1e-6, rope_cs=None,
+               out=None):
+    """x [B, T, 7168] bf16 -> (qa [B, T, 1536], qr [B, T, 1536], q [B, T, 128, 192]) bf16:
+    wq_a, q_norm, wq_b and the rotary of each head's features 128..191 at positions start_pos..
+    `out` = (qa, qr, q) reuses caller buffers."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, 7168]")
+    B, T, _ = x.shape
+    _need(x, "x", torch.bfloat16, (B, T, HIDDEN))
+    _need(w_qa, "w_qa", torch.bfloat16, (Q_LORA, HIDDEN))
+    _need(q_gain, "q_gain", torch.float32, (Q_LORA,))
+    _need(w_qb, "w_qb", torch.bfloat16, (HEADS * QK_HEAD, Q_LORA))
+    rope_cs = _positions_table(rope_cs, start_pos, T, x.device)
+    dev = x.device
+    if out is None:
+        out = (torch.empty((B, T, Q_LORA), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, Q_LORA), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, HEADS, QK_HEAD), dtype=torch.bfloat16, device=dev))
+    qa, qr, q = out
+    _need(qa, "qa", torch.bfloat16, (B, T, Q_LORA))
+    _need(qr, "qr", torch.bfloat16, (B, T, Q_LORA))
+    _need(q, "q", torch.bfloat16, (B, T, HEADS, QK_HEAD))
+    with torch.cuda.device(dev):
+        _check(lib().mla_q_path(_ptr(x), _ptr(w_qa), _ptr(q_gain), eps, _ptr(w_qb), _ptr(rope_cs),
+                                B, T, start_pos, Q_LORA, _ptr(qa), _ptr(qr), _ptr(q), _stream(dev)))
+    return qa, qr, q
 
 
 def mla_kv_up(c_kv, w_ukv, out=None):

@@ -45,23 +45,38 @@ constexpr int SB = XB + BN * ROWB;           // bytes per stage
 constexpr int XL = 32 / RPL, WL = 48 / RPL;  // 1 KB loads per wave per chunk (X rows 32w.., W rows 48w..)
 constexpr int LOADS = XL + WL;
 constexpr int KS = BK / 16;                  // MFMA k-steps per chunk
-constexpr int NK = kHidden / BK;
-constexpr int NTILES = kKvAOut / BN;         // 3
-static_assert(NK > STAGES + 1 && STAGES >= 2 && KS >= 2, "ring shape");
+constexpr int GM = 4;                        // M tiles per group in the grouped tile order
+static_assert(STAGES >= 2 && KS >= 2, "ring shape");
 static_assert(STAGES * SB <= 160 * 1024 && STAGES * SB >= BM * 384, "LDS budget");
 __device__ __forceinline__ int key(int r) { return (r / RPG) % CPR; }
 }
 
+// KD = K (row length of X and W), ND = N (row length of the output, a multiple of 192).
+template <int KD, int ND>
 __global__ __launch_bounds__(256) void gemm_down_kernel(const uint16_t* __restrict__ X,
                                                         const uint16_t* __restrict__ W, int M,
                                                         int mtiles, uint16_t* __restrict__ out) {
     using namespace down;
+    constexpr int NK = KD / BK;
+    constexpr int NTILES = ND / BN;
+    static_assert(KD % BK == 0 && ND % BN == 0 && NK > STAGES + 1, "GEMM shape");
     __shared__ __attribute__((aligned(16))) uint8_t ring[STAGES * SB];
 
-    // The three N tiles of one M tile land on the same XCD (workgroups are dealt to the 8 XCDs
-    // round-robin), so the shared X rows are fetched once per XCD L2.
+    // Workgroups are dealt to the 8 XCDs round-robin; XCD x takes the M tiles mt = x (mod 8).
+    // Few N tiles (the key-value projection's 3): all N tiles of one M tile run on the same XCD,
+    // so the shared X rows are fetched once per XCD L2. Many N tiles: groups of GM M tiles, N
+    // tile by N tile, so the ~32 workgroups resident on an XCD share GM X tiles and about 8 W
+    // tiles in its L2 instead of streaming every W tile once per M tile.
     const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
-    const int nt = j % NTILES, mt = (j / NTILES) * 8 + xcd;
+    int nt, mt;
+    if constexpr (NTILES <= 4) {
+        nt = j % NTILES;
+        mt = (j / NTILES) * 8 + xcd;
+    } else {
+        const int g = j / (GM * NTILES), idx = j - g * (GM * NTILES);
+        nt = idx / GM;
+        mt = (g * GM + idx % GM) * 8 + xcd;
+    }
     if (mt >= mtiles) return;
     const int m0 = mt * BM, n0 = nt * BN;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -76,15 +91,15 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(const uint16_t* __restri
 #pragma unroll
     for (int jj = 0; jj < XL; ++jj) {
         const int r = 32 * wave + RPL * jj + lane / CPR;
-        x_voff[jj] = (uint32_t)((min(m0 + r, M - 1) - m0) * (kHidden * 2) + ((pc ^ key(r)) << 4));
+        x_voff[jj] = (uint32_t)((min(m0 + r, M - 1) - m0) * (KD * 2) + ((pc ^ key(r)) << 4));
     }
 #pragma unroll
     for (int jj = 0; jj < WL; ++jj) {
         const int r = 48 * wave + RPL * jj + lane / CPR;
-        w_voff[jj] = (uint32_t)(r * (kHidden * 2) + ((pc ^ key(r)) << 4));
+        w_voff[jj] = (uint32_t)(r * (KD * 2) + ((pc ^ key(r)) << 4));
     }
-    const uint16_t* xg = X + (size_t)m0 * kHidden;
-    const uint16_t* wgp = W + (size_t)n0 * kHidden;
+    const uint16_t* xg = X + (size_t)m0 * KD;
+    const uint16_t* wgp = W + (size_t)n0 * KD;
     auto issue = [&](int kc, uint8_t* st) {
 #pragma unroll
         for (int jj = 0; jj < XL; ++jj) dma16(xg + kc * BK, x_voff[jj], st + (32 * wave + RPL * jj) * ROWB);
@@ -198,16 +213,27 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int idx = i * 256 + tid, row = idx / 24, c = idx - row * 24;
-        if (m0 + row < M) store16(out + (size_t)(m0 + row) * kKvAOut + n0 + c * 8, v[i]);
+        if (m0 + row < M) store16(out + (size_t)(m0 + row) * ND + n0 + c * 8, v[i]);
     }
 }
 
+namespace {
+template <int KD, int ND>
+hipError_t launch_gemm_down_form(const uint16_t* x, const uint16_t* w, int M, uint16_t* out,
+                                 hipStream_t stream) {
+    constexpr int NTILES = ND / down::BN;
+    const int mtiles = (M + down::BM - 1) / down::BM;
+    const int per_xcd = (mtiles + 7) / 8;               // M tiles of each XCD
+    const int slots = NTILES <= 4 ? per_xcd : ((per_xcd + down::GM - 1) / down::GM) * down::GM;
+    const dim3 grid(slots * 8 * NTILES);
+    gemm_down_kernel<KD, ND><<<grid, 256, 0, stream>>>(x, w, M, mtiles, out);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, uint16_t* kv_raw,
                                hipStream_t stream) {
-    const int mtiles = (M + down::BM - 1) / down::BM;
-    const dim3 grid(((mtiles + 7) / 8) * 8 * down::NTILES);
-    gemm_down_kernel<<<grid, 256, 0, stream>>>(x, w_dkv, M, mtiles, kv_raw);
-    return hipGetLastError();
+    return launch_gemm_down_form<kHidden, kKvAOut>(x, w_dkv, M, kv_raw, stream);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -269,6 +269,39 @@ int mla_window_kv(const void* kv_raw, int B, int S, int start_pos, const float* 
         static_cast<uint16_t*>(window_cache), static_cast<hipStream_t>(stream)));
 }
 
+int mla_q_path(const void* x, const void* w_qa, const float* q_gain, float eps, const void* w_qb,
+               const float* rope_cs, int B, int T, int start_pos, int q_rank, void* qa, void* qr,
+               void* q, void* stream) {
+    if (!x || !w_qa || !q_gain || !w_qb || !rope_cs || !qa || !qr || !q) return MLA_E_NULL;
+    int st = validate_positions(B, T, start_pos, 0, eps);
+    if (st != MLA_OK) return st;
+    if (q_rank != MLA_Q_LORA) return MLA_E_SHAPE;
+    if (!aligned16(x) || !aligned16(w_qa) || !aligned16(q_gain) || !aligned16(w_qb) ||
+        !aligned16(rope_cs) || !aligned16(qa) || !aligned16(qr) || !aligned16(q))
+        return MLA_E_ALIGN;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{x, M * MLA_HIDDEN * kBf16},
+                        {w_qa, (size_t)MLA_Q_LORA * MLA_HIDDEN * kBf16},
+                        {q_gain, MLA_Q_LORA * sizeof(float)},
+                        {w_qb, (size_t)MLA_HEADS * MLA_QK_HEAD * MLA_Q_LORA * kBf16},
+                        {rope_cs, (size_t)(start_pos + T) * 64 * sizeof(float)}};
+    const Span outs[] = {{qa, M * MLA_Q_LORA * kBf16},
+                         {qr, M * MLA_Q_LORA * kBf16},
+                         {q, M * MLA_HEADS * MLA_QK_HEAD * kBf16}};
+    if (any_alias(outs, 3, ins, 5)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(mla::launch_gemm_q_a(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qa),
+                                       (int)M, static_cast<uint16_t*>(qa), s));
+    if (st != MLA_OK) return st;
+    st = launched(mla::launch_rms_norm_q(static_cast<const uint16_t*>(qa), (int)M, q_gain, eps,
+                                         static_cast<uint16_t*>(qr), s));
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_gemm_q_b_rope(static_cast<const uint16_t*>(qr),
+                                              static_cast<const uint16_t*>(w_qb), (int)M,
+                                              static_cast<uint16_t*>(q), rope_cs, T, start_pos, s));
+}
+
 int mla_rope_table(int T, float theta, float* rope_cs, void* stream) {
     if (!rope_cs) return MLA_E_NULL;
     if (T < 1 || T > MLA_MAX_ROWS) return MLA_E_SHAPE;

@@ -22,6 +22,7 @@ constexpr int kNope = 128;
 constexpr int kQkHead = 192;
 constexpr int kVHead = 128;
 constexpr int kKvBOut = 32768;
+constexpr int kQRank = 1536;     // q_lora_rank (not on the pages; the library's fixed reading)
 
 // bf16 storage <-> fp32 (exact widening).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -23,6 +23,14 @@ hipError_t launch_window_kv(const uint16_t* kv_raw, int B, int S, int start_pos,
                             uint16_t* out, uint16_t* pre, uint16_t* cache, hipStream_t stream);
 hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, uint16_t* kv_raw,
                                hipStream_t stream);
+// Query path: x . W_qa^T (7168 -> 1536), the query RMSNorm, then qr . W_qb^T (1536 -> 128 x 192)
+// with the rotary part of every head rotated at position start_pos + (row % T).
+hipError_t launch_gemm_q_a(const uint16_t* x, const uint16_t* w_qa, int M, uint16_t* qa,
+                           hipStream_t stream);
+hipError_t launch_gemm_q_b_rope(const uint16_t* qr, const uint16_t* w_qb, int M, uint16_t* q,
+                                const float* rope_cs, int T, int start_pos, hipStream_t stream);
+hipError_t launch_rms_norm_q(const uint16_t* qa, int rows, const float* gain, float eps,
+                             uint16_t* qr, hipStream_t stream);
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
                              hipStream_t stream);
 // Selection bitmap [B][Wout][Tout] (Wout >= ceil(T/32), Tout >= T; the excess is zero-filled).

@@ -264,3 +264,27 @@ def test_window_kv_validation():
     assert call(out=RAW) == -8
     assert call(pre=OUT) == -8
     assert call(wc=CS) == -8
+
+
+def test_q_path_validation():
+    lib = _lib()
+    MB = 1 << 27
+    X, WA, G_, WB, CS, QA, QR, Q = (MB * i for i in range(1, 9))
+    ok = dict(x=X, wa=WA, g=G_, eps=1e-6, wb=WB, cs=CS, B=2, T=16, sp=3, r=1536, qa=QA, qr=QR, q=Q)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.mla_q_path(a["x"], a["wa"], a["g"], a["eps"], a["wb"], a["cs"], a["B"], a["T"],
+                              a["sp"], a["r"], a["qa"], a["qr"], a["q"], NOSTREAM)
+    assert call() == -5
+    assert call(x=None) == -1
+    assert call(wb=None) == -1
+    assert call(q=None) == -1
+    assert call(B=0) == -2
+    assert call(sp=-1) == -2
+    assert call(r=1024) == -2                          # q_lora_rank is fixed at 1536
+    assert call(qr=QR + 2) == -3
+    assert call(eps=0.0) == -7
+    assert call(qa=X) == -8
+    assert call(q=QR + 64) == -8
+    assert call(cs=Q) == -8
