@@ -270,6 +270,30 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
                             size_t ws_bytes, void* stream);
 
 /*
+ * mla_sparse_prefill_attn in two calls, so that the selection step (which depends only on the
+ * top-k indices) can run on another stream while the projections run:
+ * mla_attn_prepare builds the selection bitmap (the excerpt's index mask intersected with the
+ * causal mask, in the attention kernel's layout) into the workspace; it reads only topk.
+ *   topk, B, T, K       as for mla_sparse_prefill_attn.
+ *   workspace, ws_bytes (device, out) at least mla_attn_workspace_bytes(B, T, K) bytes.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ALIAS, MLA_E_DEVICE,
+ *         MLA_E_LAUNCH.
+ */
+int mla_attn_prepare(const int32_t* topk, int B, int T, int K, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * The attention of mla_sparse_prefill_attn from a workspace that mla_attn_prepare filled for the
+ * same B and T (the caller orders the two calls, e.g. with an event when they run on different
+ * streams; the workspace is only read here). Arguments as for mla_sparse_prefill_attn.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ARG, MLA_E_ALIAS,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_sparse_prefill_attn_prepared(const void* q, const void* kv, const void* k_pe, int B, int T,
+                                     float softmax_scale, void* out, const void* workspace,
+                                     size_t ws_bytes, void* stream);
+
+/*
  * Row stride (entries) of the selection lists: ceil(min(T, K) / 64) * 64. Returns 0 for shapes the
  * list call would reject.
  */

@@ -38,6 +38,8 @@ _SIGS = {
     "mla_attn_workspace_bytes": (_SZ, [_I, _I, _I]),
     "mla_selection_bitmap": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "mla_sparse_prefill_attn": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP, _SZ, _VP]),
+    "mla_attn_prepare": (_I, [_VP, _I, _I, _I, _VP, _SZ, _VP]),
+    "mla_sparse_prefill_attn_prepared": (_I, [_VP, _VP, _VP, _I, _I, _F, _VP, _VP, _SZ, _VP]),
     "mla_selection_list_stride": (_I, [_I, _I]),
     "mla_selection_lists": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "mla_attn_latent_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -324,6 +326,41 @@ def mla_kv_up(c_kv, w_ukv, out=None):
     _need(out, "out", torch.bfloat16, (B, HEADS, T, QK_NOPE + V_HEAD))
     with torch.cuda.device(c_kv.device):
         _check(lib().mla_kv_up(_ptr(c_kv), _ptr(w_ukv), B, T, _ptr(out), _stream(c_kv.device)))
+    return out
+
+
+def mla_attn_prepare(topk, workspace, stream=None):
+    """Selection bitmap for mla_sparse_prefill_attn_prepared, built into `workspace` (uint8,
+    at least mla_attn_workspace_bytes(B, T, K) bytes) on `stream` (default: current stream)."""
+    if topk.dim() != 3:
+        raise ValueError("topk must be [B, T, K]")
+    B, T, K = topk.shape
+    _need(topk, "topk", torch.int32)
+    _need(workspace, "workspace", torch.uint8)
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(topk.device)
+    with torch.cuda.device(topk.device):
+        _check(lib().mla_attn_prepare(_ptr(topk), B, T, K, _ptr(workspace), workspace.numel(), s))
+    return workspace
+
+
+def mla_sparse_prefill_attn_prepared(q, kv, k_pe, workspace, softmax_scale: float | None = None,
+                                     out=None):
+    """The attention of mla_sparse_prefill_attn from a workspace mla_attn_prepare filled."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, 128, 192]")
+    B, T = q.shape[0], q.shape[1]
+    _need(q, "q", torch.bfloat16, (B, T, HEADS, QK_HEAD))
+    _need(kv, "kv", torch.bfloat16, (B, HEADS, T, QK_NOPE + V_HEAD))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
+    _need(workspace, "workspace", torch.uint8)
+    scale = mla_default_softmax_scale() if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((B, T, HEADS, V_HEAD), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, HEADS, V_HEAD))
+    with torch.cuda.device(q.device):
+        _check(lib().mla_sparse_prefill_attn_prepared(_ptr(q), _ptr(kv), _ptr(k_pe), B, T, scale,
+                                                      _ptr(out), _ptr(workspace), workspace.numel(),
+                                                      _stream(q.device)))
     return out
 
 

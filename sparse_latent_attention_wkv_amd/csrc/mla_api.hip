@@ -345,16 +345,64 @@ int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bit
                                            static_cast<hipStream_t>(stream)));
 }
 
+int mla_attn_prepare(const int32_t* topk, int B, int T, int K, void* workspace, size_t ws_bytes,
+                     void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!workspace) return MLA_E_NULL;
+    if (!aligned16(workspace)) return MLA_E_ALIGN;
+    if (ws_bytes < attn_bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
+    const Span ins[] = {{topk, (size_t)B * T * K * sizeof(int32_t)}};
+    const Span outs[] = {{workspace, attn_bitmap_bytes(B, T)}};
+    if (any_alias(outs, 1, ins, 1)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
+                                           mla::attn_bitmap_cols(T), static_cast<uint32_t*>(workspace),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int validate_attn_prepared(const void* q, const void* kv, const void* k_pe, int B, int T,
+                           float softmax_scale, const void* out, const void* workspace,
+                           size_t ws_bytes) {
+    if (!q || !kv || !k_pe || !out || !workspace) return MLA_E_NULL;
+    if (B < 1 || T < 1 || T > MLA_MAX_T || (size_t)B * T > (size_t)MLA_MAX_ROWS) return MLA_E_SHAPE;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(k_pe) || !aligned16(out) || !aligned16(workspace))
+        return MLA_E_ALIGN;
+    if (!pos_finite(softmax_scale)) return MLA_E_ARG;
+    if (ws_bytes < attn_bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
+                        {kv, M * MLA_HEADS * 256 * kBf16},
+                        {k_pe, M * MLA_ROPE * kBf16},
+                        {workspace, attn_bitmap_bytes(B, T)}};
+    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}};
+    if (any_alias(outs, 1, ins, 4)) return MLA_E_ALIAS;
+    return MLA_OK;
+}
+}  // namespace
+
+int mla_sparse_prefill_attn_prepared(const void* q, const void* kv, const void* k_pe, int B, int T,
+                                     float softmax_scale, void* out, const void* workspace,
+                                     size_t ws_bytes, void* stream) {
+    int st = validate_attn_prepared(q, kv, k_pe, B, T, softmax_scale, out, workspace, ws_bytes);
+    if (st != MLA_OK) return st;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
+                                            static_cast<const uint16_t*>(kv),
+                                            static_cast<const uint16_t*>(k_pe),
+                                            static_cast<const uint32_t*>(workspace), B, T,
+                                            softmax_scale, static_cast<uint16_t*>(out),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
                             int B, int T, int K, float softmax_scale, void* out, void* workspace,
                             size_t ws_bytes, void* stream) {
     int st = validate_topk(topk, B, T, K);
     if (st != MLA_OK) return st;
-    if (!q || !kv || !k_pe || !out || !workspace) return MLA_E_NULL;
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(k_pe) || !aligned16(out) || !aligned16(workspace))
-        return MLA_E_ALIGN;
-    if (!pos_finite(softmax_scale)) return MLA_E_ARG;
-    if (ws_bytes < attn_bitmap_bytes(B, T)) return MLA_E_WORKSPACE;
+    if ((st = validate_attn_prepared(q, kv, k_pe, B, T, softmax_scale, out, workspace, ws_bytes)) != MLA_OK)
+        return st;
     const size_t M = (size_t)B * T;
     const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
                         {kv, M * MLA_HEADS * 256 * kBf16},

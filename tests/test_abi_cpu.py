@@ -288,3 +288,29 @@ def test_q_path_validation():
     assert call(qa=X) == -8
     assert call(q=QR + 64) == -8
     assert call(cs=Q) == -8
+
+
+def test_attn_prepare_and_prepared_validation():
+    lib = _lib()
+    GB = 1 << 30
+    Q, KV, KPE, TK, OUT, WS = (GB * i for i in range(1, 7))
+    ws = lib.mla_attn_workspace_bytes(2, 256, 16)
+
+    def prep(topk=TK, B=2, T=256, K=16, wk=WS, wsb=ws):
+        return lib.mla_attn_prepare(topk, B, T, K, wk, wsb, NOSTREAM)
+
+    def attn(q=Q, kv=KV, kpe=KPE, B=2, T=256, scale=0.135, out=OUT, wk=WS, wsb=ws):
+        return lib.mla_sparse_prefill_attn_prepared(q, kv, kpe, B, T, scale, out, wk, wsb, NOSTREAM)
+    assert prep() == -5 and attn() == -5
+    assert prep(topk=None) == -1 and prep(wk=None) == -1
+    assert prep(K=0) == -2 and prep(T=40000) == -2
+    assert prep(wk=WS + 4) == -3
+    assert prep(wsb=ws - 1) == -4
+    assert prep(wk=TK) == -8                           # bitmap written over the indices
+    assert attn(q=None) == -1 and attn(wk=None) == -1
+    assert attn(B=0) == -2 and attn(T=40000) == -2
+    assert attn(out=OUT + 2) == -3
+    assert attn(wsb=ws - 1) == -4
+    assert attn(scale=0.0) == -7
+    assert attn(out=KV) == -8
+    assert attn(out=WS) == -8                          # output over the prepared bitmap

@@ -273,3 +273,31 @@ def test_attention_ignores_poisoned_unselected_keys_and_index_order():
     assert np.array_equal(_run_attn(q, kv, kpe, shuffled), base)
     # bitwise deterministic
     assert np.array_equal(_run_attn(q, kv, kpe, topk), base)
+
+
+def test_prepared_attention_on_a_second_stream_matches_one_call():
+    """mla_attn_prepare on another stream (ordered with an event) followed by
+    mla_sparse_prefill_attn_prepared gives the one-call result bit for bit; a stale workspace
+    from another selection is fully overwritten."""
+    B, T, K = 2, 300, 64
+    say(f"prepared attention B={B} T={T} K={K}")
+    q, kv, k_pe, topk = _attn_inputs(4500, B, T, K)
+    qd, kvd, ped = to_dev(q), to_dev(kv), to_dev(k_pe)
+    tk = torch.from_numpy(topk).to(dev())
+    scale = mla.mla_default_softmax_scale()
+    one = mla.mla_sparse_prefill_attn(qd, kvd, ped, tk, scale)
+    ws = torch.empty(mla.mla_attn_workspace_bytes(B, T, K), dtype=torch.uint8, device=dev())
+    other = torch.from_numpy(synth.random_topk(4501, B, T, K)).to(dev())
+    mla.mla_attn_prepare(other, ws)                      # stale contents first
+    side = torch.cuda.Stream(dev())
+    main = torch.cuda.current_stream(dev())
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    mla.mla_attn_prepare(tk, ws, stream=side)
+    ready = torch.cuda.Event()
+    ready.record(side)
+    main.wait_event(ready)
+    two = mla.mla_sparse_prefill_attn_prepared(qd, kvd, ped, ws, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
