@@ -22,7 +22,8 @@
 //
 // Tile order: XCD x (workgroups are dealt to the 8 XCDs round-robin) takes the M tiles
 // mt = x (mod 8), in groups of four M tiles walked N tile by N tile, so the workgroups resident
-// on one XCD share four X tiles and a few W tiles in its L2.
+// on one XCD share four X tiles and a few W tiles in its L2. With fewer than 8 M tiles that
+// order would leave XCDs idle; the tiles then go in plain order.
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
@@ -58,10 +59,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
     static_assert(!ROPE || BN % 8 == 0, "rotary pieces");
     __shared__ __attribute__((aligned(16))) uint8_t ring[STAGES * SB];
 
-    const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
-    const int g = j / (GM * NTILES), idx = j - g * (GM * NTILES);
-    const int nt = idx / GM, mt = (g * GM + idx % GM) * 8 + xcd;
-    if (mt >= mtiles) return;
+    int nt, mt;
+    if (mtiles >= 8) {
+        const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
+        const int g = j / (GM * NTILES), idx = j - g * (GM * NTILES);
+        nt = idx / GM;
+        mt = (g * GM + idx % GM) * 8 + xcd;
+        if (mt >= mtiles) return;
+    } else {   // fewer M tiles than XCDs: plain order, so every XCD gets tiles
+        mt = blockIdx.x % mtiles;
+        nt = blockIdx.x / mtiles;
+    }
     const int m0 = mt * BM, n0 = nt * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,7 +228,8 @@ hipError_t launch_big(const uint16_t* x, const uint16_t* w, int M, uint16_t* out
     const int mtiles = (M + big::BM - 1) / big::BM;
     const int per_xcd = (mtiles + 7) / 8;
     const int slots = ((per_xcd + big::GM - 1) / big::GM) * big::GM;
-    gemm_big_kernel<KD, ND, BN, BK, STAGES, ROPE><<<dim3(slots * 8 * NTILES), 256, 0, stream>>>(
+    const int blocks = mtiles >= 8 ? slots * 8 * NTILES : mtiles * NTILES;
+    gemm_big_kernel<KD, ND, BN, BK, STAGES, ROPE><<<dim3(blocks), 256, 0, stream>>>(
         x, w, M, mtiles, out, rope_cs, T, start_pos);
     return hipGetLastError();
 }
