@@ -19,6 +19,7 @@ import torch
 import oracle
 import synth
 from _gpu import assert_within_one_step, bf16_step, dev, fp32_dot_bound, say, to_dev, to_host
+from _gpu import attention_close as strict_attention_close
 
 mla = pytest.importorskip("sparse_latent_attention_wkv_amd")
 
@@ -144,7 +145,8 @@ def test_latent_attention_exact_max_path():
 
 def _latent_rows_ref(q, c_kv, k_pe, w, topk, b, rows):
     """Oracle for sampled query rows of a large workload: each row's allowed keys alone, as a
-    compact problem (the keys renumbered 0..n-1 in order, the query last)."""
+    compact problem (the keys renumbered 0..n-1 in order, the query last). q: bf16 bits indexed
+    q[b, s] (an array, or any object with that indexing)."""
     res = []
     wf = f32(w)
     for s in rows:
@@ -219,3 +221,59 @@ def test_auto_long_workload_sampled():
     say(f"split {split}: checking rows {rows}")
     ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], 0, rows)
     attention_close(to_host(out[0, rows]), ref, "long split form")
+
+
+class _Rows:
+    """q[b, s] for a few rows copied from a device tensor (the full query does not fit the
+    oracle's host memory comfortably at the longest length)."""
+
+    def __init__(self, q_dev, rows):
+        self.rows = {int(s): q_dev[0, int(s)].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                     for s in rows}
+
+    def __getitem__(self, key):
+        return self.rows[int(key[1])]
+
+
+def test_longest_sequence_auto_and_head_major():
+    """T = MLA_MAX_T (32768), top-k 2048: the split form (head-major rows below the split,
+    latent rows above) and the head-major path alone, on sampled rows of both ranges."""
+    B, T, K = 1, 32768, 2048
+    say(f"longest sequence B={B} T={T} K={K}: inputs")
+    topk = synth.random_topk(4700, B, T, K)
+    ckv_bits = synth.random_bf16(4701, (B, T, 512))
+    kpe_bits = synth.random_bf16(4702, (B, T, 64))
+    w = synth.random_bf16(4703, (32768, 512), std=512 ** -0.5)
+    gen = torch.Generator(device=dev()).manual_seed(4704)
+    q = torch.randn((B, T, 128, 192), generator=gen, device=dev()).to(torch.bfloat16)
+    c_kv, k_pe, wu = to_dev(ckv_bits), to_dev(kpe_bits), to_dev(w)
+    tk = torch.from_numpy(topk).to(dev())
+    split = mla.mla_attn_auto_split(T, K)
+    assert 0 < split < T
+    say(f"  split form (split {split})")
+    out = mla.mla_sparse_prefill_attn_auto(q, c_kv, k_pe, wu, tk, SCALE)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4705)
+    rows = sorted(set([0, 1, K - 1, split - 1, split, T - 2, T - 1] + rng.integers(0, T, 3).tolist()))
+    qr = _Rows(q, rows)
+    ref = _latent_rows_ref(qr, ckv_bits, kpe_bits, w, topk, 0, rows)
+    attention_close(to_host(out[0, rows]), ref, "longest sequence, split form")
+    say("  head-major path")
+    kv = mla.mla_kv_up(c_kv, wu)
+    out_hm = mla.mla_sparse_prefill_attn(q, kv, k_pe, tk, SCALE)
+    torch.cuda.synchronize()
+    # reference from the GPU's own keys and values (the head-major criterion of the pages'
+    # tolerances: rel-L2 <= 1e-2, max-abs <= 2e-2)
+    ref_hm = []
+    for s_ in rows:
+        ids = np.asarray(topk[0, s_]).astype(np.int64)
+        ids = np.unique(ids[(ids >= 0) & (ids <= s_)])
+        n = len(ids)
+        kv_c = to_host(kv[0][:, torch.from_numpy(ids).to(dev())])[None]        # [1, H, n, 256]
+        q_c = np.zeros((1, n, 128, 192), np.float32)
+        q_c[0, n - 1] = f32(qr[0, s_])
+        topk_c = np.full((1, n, n), -1, np.int32)
+        topk_c[0, n - 1] = np.arange(n)
+        ref_hm.append(oracle.sparse_prefill_attn_rows(q_c, kv_c, f32(kpe_bits[0:1, ids]), topk_c,
+                                                      SCALE, 0, [n - 1])[0])
+    strict_attention_close(to_host(out_hm[0, rows]), np.stack(ref_hm), "longest sequence, head-major")
