@@ -31,11 +31,12 @@ namespace mla {
 // quotient and the correctly rounded reciprocal, one more step gives the correctly rounded
 // quotient (Markstein's theorem on division by fused multiply-add). Valid while nothing over- or
 // underflows: callers keep s >= 2^-100, and |x / s| <= 464; quotients in the fp32 subnormal range
-// are far below the smallest e4m3 step and become code 0 either way.
+// are far below the smallest e4m3 step and become code 0 either way. The remainder steps turn a
+// quotient of -0 into +0; the sign of x (s > 0) is put back, as the division keeps it.
 __device__ __forceinline__ float quotient_rn(float x, float s, float rc) {
     const float y0 = x * rc;
     const float y1 = fmaf(fmaf(-s, y0, x), rc, y0);
-    return fmaf(fmaf(-s, y1, x), rc, y1);
+    return copysignf(fmaf(fmaf(-s, y1, x), rc, y1), x);
 }
 
 // Two quotients to their nearest e4m3 values (round to nearest even, the finite-only e4m3 format

@@ -42,6 +42,7 @@ def _spice(x_bits, seed):
     rng = np.random.default_rng(seed)
     if n >= 3:
         x[0, 0:128] = 0.0
+        x[0, 128:136] = -0.0                                  # signed zeros keep their sign
         x[1, 128:256] *= np.where(rng.random(128) < 0.9, 1e-4, 1.0)
         x[2, :512] = 0.0
     return synth.f32_to_bf16_bits(x)
@@ -49,6 +50,13 @@ def _spice(x_bits, seed):
 
 def _check_pre(got, ref, what):
     assert_within_one_step(got, ref, what=what)
+
+
+def same_bits(a, b):
+    """Bit-for-bit equality of two float32 arrays of bf16 values (signed zeros included)."""
+    a = np.ascontiguousarray(a, np.float32)
+    b = np.ascontiguousarray(b, np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 # ------------------------------------------------------------------------------ f2
@@ -84,11 +92,11 @@ def test_kv_latent_cache_matches_oracle(B, T, sp, fmt, cb, cl):
     mag = np.hypot(pe[..., 0::2].astype(np.float64), pe[..., 1::2].astype(np.float64)).repeat(2, -1)
     assert_within_one_step(kpe, ref, extra=4 * 2.0 ** -24 * mag, what="k_pe")
     # the round trip, bit for bit
-    assert np.array_equal(ckv, f8.fp8_round_trip(cn, FMT[fmt])), "c_kv round trip"
+    assert same_bits(ckv, f8.fp8_round_trip(cn, FMT[fmt])), "c_kv round trip"
     # cache rows, bit for bit; rows outside the call untouched
     want_kc, want_pc = f8.cache_write(ckv, kpe, f32(kc0), f32(pc0), sp)
-    assert np.array_equal(to_host(kc), want_kc), "kv_cache"
-    assert np.array_equal(to_host(pc), want_pc), "pe_cache"
+    assert same_bits(to_host(kc), want_kc), "kv_cache"
+    assert same_bits(to_host(pc), want_pc), "pe_cache"
 
 
 def test_norm_rope_cache_step_alone_and_without_c_norm():
@@ -106,16 +114,16 @@ def test_norm_rope_cache_step_alone_and_without_c_norm():
     cn = to_host(c_norm)
     _check_pre(cn, oracle.rms_norm(f32(raw_bits)[..., :512], gain), "c_norm")
     got = to_host(c_kv)
-    assert np.array_equal(got, f8.fp8_round_trip(cn))
+    assert same_bits(got, f8.fp8_round_trip(cn))
     assert not got[0, 0, :128].any() and not got[0, 2, :].any()       # zero block, zero row
-    assert np.array_equal(got, to_host(c_kv2)) and np.array_equal(to_host(k_pe), to_host(k_pe2))
+    assert same_bits(got, to_host(c_kv2)) and same_bits(to_host(k_pe), to_host(k_pe2))
     assert torch.equal(kc, kc2) and torch.equal(pc, pc2)
     # the unfused norm/rotary kernel gives the same normalised latent and rotated key
     flat = raw.reshape(B * T, 576)
     cs = mla.mla_rope_table(sp + T, dev())[sp:].contiguous()
     c_plain, k_plain = mla.mla_kv_norm_rope(flat, g, 1e-6, cs, T)
     torch.cuda.synchronize()
-    assert np.array_equal(to_host(c_plain).reshape(B, T, 512), cn)
+    assert same_bits(to_host(c_plain).reshape(B, T, 512), cn)
     assert_within_one_step(to_host(k_pe), to_host(k_plain).reshape(B, T, 64), what="k_pe vs plain")
 
 
@@ -137,9 +145,9 @@ def test_norm_rope_cache_front_end_workload_rows():
     _check_pre(cn.reshape(-1, 512)[rows],
                oracle.rms_norm(f32(raw_bits).reshape(-1, 576)[rows, :512], gain), "c_norm rows")
     ckv = to_host(c_kv)
-    assert np.array_equal(ckv, f8.fp8_round_trip(cn))
-    assert np.array_equal(to_host(kc), ckv)
-    assert np.array_equal(to_host(pc), to_host(k_pe))
+    assert same_bits(ckv, f8.fp8_round_trip(cn))
+    assert same_bits(to_host(kc), ckv)
+    assert same_bits(to_host(pc), to_host(k_pe))
 
 
 # ------------------------------------------------------------------------------ f4
@@ -175,8 +183,8 @@ def test_window_kv_matches_oracle(B, S, sp, W, fmt):
     pair = bf16_step(re) + bf16_step(im) + 4 * 2.0 ** -24 * np.hypot(re, im)
     extra[..., 448:] = pair.repeat(2, -1)
     assert_within_one_step(preh, ref_pre, extra=extra, what="kv_pre")
-    assert np.array_equal(kvh, f8.fp8_round_trip(preh, FMT[fmt])), "round trip"
-    assert np.array_equal(to_host(cache), f8.ring_write(kvh, f32(cache0), sp)), "ring buffer"
+    assert same_bits(kvh, f8.fp8_round_trip(preh, FMT[fmt])), "round trip"
+    assert same_bits(to_host(cache), f8.ring_write(kvh, f32(cache0), sp)), "ring buffer"
 
 
 def test_window_prefill_then_decode_steps():
@@ -193,9 +201,9 @@ def test_window_prefill_then_decode_steps():
     kv = mla.mla_window_kv(to_dev(raw_bits[:, :S0]), g, cache, start_pos=0, rope_cs=cs)
     torch.cuda.synchronize()
     want = f8.ring_write(to_host(kv), want, 0)
-    assert np.array_equal(to_host(cache), want)
+    assert same_bits(to_host(cache), want)
     for p in range(S0, S0 + 12):
         kv = mla.mla_window_kv(to_dev(raw_bits[:, p:p + 1]), g, cache, start_pos=p, rope_cs=cs)
         torch.cuda.synchronize()
         want = f8.ring_write(to_host(kv), want, p)
-        assert np.array_equal(to_host(cache), want), f"after decode position {p}"
+        assert same_bits(to_host(cache), want), f"after decode position {p}"
