@@ -163,7 +163,17 @@ def side_measurements(torch, mla, dev, stream, topk, B: int, T: int, K: int) -> 
     w_bytes = 3072.0 * 256
     window = {"rows": 256, "us": us_w, "GB_s": w_bytes / (us_w * 1e-6) / 1e9, "bytes": w_bytes}
     del kv_raw, c_kv, k_pe, bm, kc, pc, wraw, wcache, wout
+    # The front-end workload's decode variant: 256 rows of 512, RMSNorm eps 1e-20, no rotary
+    # (1024 B read + 1024 B written per row; launch-bound), through the C entry point.
+    draw = torch.randn((256, 512), device=dev).to(torch.bfloat16)
+    dout = torch.empty((256, 512), dtype=torch.bfloat16, device=dev)
+    mla.mla_kv_norm_rope(draw, gain, 1e-20, out=(dout, None))                       # checks once
+    dargs = (P(draw), 256, 512, 0, P(gain), 1e-20, None, 1, P(dout), None,
+             ctypes.c_void_p(stream.cuda_stream))
+    us_d = timed_us(torch, stream, lambda: L.mla_kv_norm_rope(*dargs), reps=200, warm=20)
+    decode = {"rows": 256, "us": us_d, "GB_s": 2048.0 * 256 / (us_d * 1e-6) / 1e9, "bytes": 2048.0 * 256}
     side = {"norm_rope_frontend_B8_T4096": norm, "selection_bitmap": bitmap,
+            "norm_decode_B256_eps1e-20": decode,
             "norm_rope_fp8_cache_B8_T4096": cache, "window_kv_decode_B256": window}
     side["query_path"] = query_path_measurement(torch, mla, dev, stream, B, T)
     return side
