@@ -20,10 +20,13 @@
 // features 128..191 of each 192-wide query head are rotated there, after the bf16 rounding of the
 // product, at position start_pos + (row % T) (the query path's rotary step).
 //
-// Tile order: XCD x (workgroups are dealt to the 8 XCDs round-robin) takes the M tiles
-// mt = x (mod 8), in groups of four M tiles walked N tile by N tile, so the workgroups resident
-// on one XCD share four X tiles and a few W tiles in its L2. With fewer than 8 M tiles that
-// order would leave XCDs idle; the tiles then go in plain order.
+// Tile order: tile slot w goes to XCD w mod 8 (workgroups are dealt to the 8 XCDs round-robin,
+// and a persistent workgroup keeps its XCD, stepping through slots by the grid size, a multiple
+// of 8); XCD x takes the M tiles mt = x (mod 8), in groups of four M tiles walked N tile by N
+// tile, so the workgroups resident on one XCD share four X tiles and a few W tiles in its L2.
+// With fewer than 8 M tiles that order would leave XCDs idle; the tiles then go in plain order.
+// At most one workgroup per compute unit (256) is launched; each runs its tiles one after
+// another (2% faster than one workgroup per tile at 8192 tokens: no relaunch between tiles).
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ W, int M,
                                                        int mtiles, uint16_t* __restrict__ out,
                                                        const float* __restrict__ rope_cs, int T,
-                                                       int start_pos) {
+                                                       int start_pos, int nslots) {
     using namespace big;
     constexpr int ROWB = BK * 2;                 // bytes per LDS row
     constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
@@ -59,16 +62,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
     static_assert(!ROPE || BN % 8 == 0, "rotary pieces");
     __shared__ __attribute__((aligned(16))) uint8_t ring[STAGES * SB];
 
+    for (int wg = blockIdx.x; wg < nslots; wg += gridDim.x) {
     int nt, mt;
     if (mtiles >= 8) {
-        const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
+        const int xcd = wg & 7, j = wg >> 3;
         const int g = j / (GM * NTILES), idx = j - g * (GM * NTILES);
         nt = idx / GM;
         mt = (g * GM + idx % GM) * 8 + xcd;
-        if (mt >= mtiles) return;
+        if (mt >= mtiles) continue;
     } else {   // fewer M tiles than XCDs: plain order, so every XCD gets tiles
-        mt = blockIdx.x % mtiles;
-        nt = blockIdx.x / mtiles;
+        mt = wg % mtiles;
+        nt = wg / mtiles;
     }
     const int m0 = mt * BM, n0 = nt * BN;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -213,6 +217,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
         }
         store16(out + (size_t)(m0 + row) * ND + n0 + c * 8, v);
     }
+    __syncthreads();   // the ring's staging reads are done before the next tile's loads land
+    }
 }
 
 // 64-deep chunks in two stages: measured against 32-deep chunks in four stages (three chunks of
@@ -229,8 +235,9 @@ hipError_t launch_big(const uint16_t* x, const uint16_t* w, int M, uint16_t* out
     const int per_xcd = (mtiles + 7) / 8;
     const int slots = ((per_xcd + big::GM - 1) / big::GM) * big::GM;
     const int blocks = mtiles >= 8 ? slots * 8 * NTILES : mtiles * NTILES;
-    gemm_big_kernel<KD, ND, BN, BK, STAGES, ROPE><<<dim3(blocks), 256, 0, stream>>>(
-        x, w, M, mtiles, out, rope_cs, T, start_pos);
+    const int grid = blocks < 256 ? blocks : 256;   // a multiple of 8 when it is 256
+    gemm_big_kernel<KD, ND, BN, BK, STAGES, ROPE><<<dim3(grid), 256, 0, stream>>>(
+        x, w, M, mtiles, out, rope_cs, T, start_pos, blocks);
     return hipGetLastError();
 }
 }  // namespace
