@@ -247,6 +247,25 @@ size_t mla_attn_workspace_bytes(int B, int T, int K);
 int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bitmap, void* stream);
 
 /*
+ * Validity report of a top-k selection (a debug aid; the attention calls never need it). The
+ * MHA-prefill code excerpt of "DeepSeek-V3.2-Exp · Keys" scatters the indexer's top-k indices into
+ * a -inf index mask and adds the causal mask; the attention calls read each entry the same way
+ * (outside [0, T): selects nothing, -1 marking an empty slot; later than the query: removed by the
+ * causal mask; repeated: selected once), so no entry is an error to them and none is reported by
+ * them. This call counts, over all B * T rows:
+ *   counts[0]  entries outside [-1, T) (neither a key position nor the empty-slot marker),
+ *   counts[1]  entries t with s < t < T (later than their query s),
+ *   counts[2]  repeats of an allowed entry within its row (each occurrence after the first),
+ *   counts[3]  rows whose allowed set is empty (the attention calls write zeros for such a row).
+ *   topk    (device) int32 [B, T, K], as for mla_selection_bitmap.
+ *   counts  (device, out) int64 [4], overwritten. The call is asynchronous like every other:
+ *           synchronise the stream before reading the counts.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (as mla_selection_bitmap), MLA_E_ALIGN, MLA_E_ALIAS,
+ *         MLA_E_DEVICE, MLA_E_LAUNCH.
+ */
+int mla_check_topk(const int32_t* topk, int B, int T, int K, int64_t* counts, void* stream);
+
+/*
  * Sparse prefill attention.
  *   q        (device) bf16 [B, T, 128, 192], each head's query as [128 non-rotary | 64 rotary]
  *            (the excerpt concatenates q_nope and q_pe in that order).
@@ -260,8 +279,8 @@ int mla_selection_bitmap(const int32_t* topk, int B, int T, int K, uint32_t* bit
  *            Keys outside A(b,s) receive exactly zero weight.
  *   workspace, ws_bytes  (device) scratch of at least mla_attn_workspace_bytes(B, T, K) bytes;
  *            its contents on entry do not matter and are overwritten.
- * Precondition (not checked): every query has at least one allowed key (the workloads always
- * select the query's own position); an empty row yields NaN, as the pages' form does.
+ * A query with no allowed key (outside the pages' contract: their -inf mask would give NaN there)
+ * gets an output row of zeros; mla_check_topk counts such rows.
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ARG, MLA_E_ALIAS,
  *         MLA_E_DEVICE, MLA_E_LAUNCH.
  */
@@ -336,7 +355,7 @@ size_t mla_attn_latent_workspace_bytes(int B, int T, int K);
  *   softmax_scale, out  as for mla_sparse_prefill_attn (out [B, T, 128, 128] bf16).
  *   workspace, ws_bytes  (device) at least mla_attn_latent_workspace_bytes(B, T, K) bytes,
  *            contents on entry irrelevant.
- * Same precondition as mla_sparse_prefill_attn (an empty row yields NaN).
+ * As for mla_sparse_prefill_attn, a query with no allowed key gets an output row of zeros.
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ARG, MLA_E_ALIAS,
  *         MLA_E_DEVICE, MLA_E_LAUNCH.
  */

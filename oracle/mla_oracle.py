@@ -174,18 +174,25 @@ def kv_latent(x, w_dkv, gain, eps: float = RMS_EPS_DEFAULT, theta: float = ROPE_
 
 
 # --- 4. key-value up-projection --------------------------------------------------------------------
-def kv_up(c_kv, w_ukv, n_heads: int = N_HEADS) -> np.ndarray:
+def kv_up(c_kv, w_ukv, n_heads: int = N_HEADS, rounded: bool = True) -> np.ndarray:
     """kv[b, h, t, :] = bf16(c_kv[b, t] @ W_UKV^T)[h*256:(h+1)*256]; features 0..127 of a head
     are its non-rotary key, 128..255 its value (MHA-prefill excerpt: view to
     [B, T, heads, 256] then split [128, 128]; Keys and Split value heads pages: head-major
-    shapes [B, 128, T, .]). Returns [B, H, T, 256]."""
+    shapes [B, 128, T, .]). Returns [B, H, T, 256] float32 (bf16 values).
+
+    ``rounded=False`` returns the float64 products without the bf16 rounding. The per-head
+    keys and values are a stored module output only where something stores them; a
+    computation that regroups the products around the latent never forms them, and its
+    reference is the same arithmetic with this rounding left out (float64 result)."""
     c = np.asarray(c_kv, np.float64)
     w = np.asarray(w_ukv, np.float64)
     B, T, _ = c.shape
     per = w.shape[0] // n_heads
-    out = np.empty((B, n_heads, T, per), np.float32)
+    out = np.empty((B, n_heads, T, per), np.float32 if rounded else np.float64)
     for b in range(B):
-        y = bf16(c[b] @ w.T)                       # [T, H*per]
+        y = c[b] @ w.T                             # [T, H*per]
+        if rounded:
+            y = bf16(y)
         out[b] = y.reshape(T, n_heads, per).transpose(1, 0, 2)
     return out
 
@@ -208,6 +215,28 @@ def selection_mask(topk, T: int) -> np.ndarray:
         allowed[b, rows[ok], cols[ok]] = True
     allowed &= np.tril(np.ones((T, T), dtype=bool))
     return allowed
+
+
+def topk_defects(topk, T: int) -> dict:
+    """Counts over a selection [B, T, K] of the entries the index mask reads in a special way
+    (MHA-prefill excerpt: the indexer's indices are scattered into a -inf mask, which gives
+    repeated indices set semantics, and the causal mask removes later positions; -1 marks an
+    empty slot in this library's reading of the index format):
+    ``invalid`` entries outside [-1, T), ``future`` entries t with s < t < T, ``repeated``
+    occurrences of an allowed entry after its first in the row, ``empty_rows`` queries whose
+    allowed set is empty."""
+    topk = np.asarray(topk).astype(np.int64)
+    B, Tq, K = topk.shape
+    if Tq != T:
+        raise ValueError("topk must have one row per query")
+    s = np.arange(T)[None, :, None]
+    invalid = (topk < -1) | (topk >= T)
+    future = (topk > s) & (topk < T)
+    allowed_entry = (topk >= 0) & (topk <= s)
+    n_allowed = int(allowed_entry.sum())
+    distinct = selection_mask(topk, T).sum(axis=-1)          # [B, T]
+    return {"invalid": int(invalid.sum()), "future": int(future.sum()),
+            "repeated": n_allowed - int(distinct.sum()), "empty_rows": int((distinct == 0).sum())}
 
 
 def _keys(kv, k_pe, b, h):

@@ -40,6 +40,7 @@ _SIGS = {
     "mla_sparse_prefill_attn": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP, _SZ, _VP]),
     "mla_attn_prepare": (_I, [_VP, _I, _I, _I, _VP, _SZ, _VP]),
     "mla_sparse_prefill_attn_prepared": (_I, [_VP, _VP, _VP, _I, _I, _F, _VP, _VP, _SZ, _VP]),
+    "mla_check_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "mla_selection_list_stride": (_I, [_I, _I]),
     "mla_selection_lists": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "mla_attn_latent_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -135,6 +136,9 @@ def mla_kv_latent(x, w_dkv, kv_gain, eps: float = 1e-6, rope_cs=None, out=None):
                torch.empty((B, T, KV_LORA), dtype=torch.bfloat16, device=x.device),
                torch.empty((B, T, ROPE), dtype=torch.bfloat16, device=x.device))
     kv_raw, c_kv, k_pe = out
+    _need(kv_raw, "kv_raw", torch.bfloat16, (B, T, KV_A_OUT))
+    _need(c_kv, "c_kv", torch.bfloat16, (B, T, KV_LORA))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
     with torch.cuda.device(x.device):
         _check(lib().mla_kv_latent(_ptr(x), _ptr(w_dkv), _ptr(kv_gain), eps, _ptr(rope_cs), B, T,
                                    _ptr(kv_raw), _ptr(c_kv), _ptr(k_pe), _stream(x.device)))
@@ -379,6 +383,23 @@ def mla_selection_bitmap(topk, out=None):
     with torch.cuda.device(topk.device):
         _check(lib().mla_selection_bitmap(_ptr(topk), B, T, K, _ptr(bm), _stream(topk.device)))
     return bm
+
+
+def mla_check_topk(topk, out=None):
+    """topk [B, T, K] int32 -> dict of counts: entries outside [-1, T) ("invalid"), entries later
+    than their query ("future"), repeats of an allowed entry within a row ("repeated"), rows with
+    no allowed key ("empty_rows"). Reads the counts back, which waits for the call. `out` reuses
+    a device int64 [4] buffer."""
+    if topk.dim() != 3:
+        raise ValueError("topk must be [B, T, K]")
+    B, T, K = topk.shape
+    _need(topk, "topk", torch.int32)
+    counts = torch.empty(4, dtype=torch.int64, device=topk.device) if out is None else out
+    _need(counts, "counts", torch.int64, (4,))
+    with torch.cuda.device(topk.device):
+        _check(lib().mla_check_topk(_ptr(topk), B, T, K, _ptr(counts), _stream(topk.device)))
+    c = counts.cpu().tolist()
+    return {"invalid": c[0], "future": c[1], "repeated": c[2], "empty_rows": c[3]}
 
 
 def mla_sparse_prefill_attn(q, kv, k_pe, topk, softmax_scale: float | None = None,

@@ -408,9 +408,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     }
 
     // Epilogue: the two lane halves hold partial sums over different keys of the same query.
+    // A query with no allowed key has l_tot = 0 and o = 0: its row is written as zeros.
     const float l_tot = half_sum(l_run);
     if (qrow < T) {
-        const float inv = 1.0f / l_tot;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         uint16_t* dst = out + (((size_t)b * T + qrow) * kHeads + h) * kVHead;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)

@@ -615,8 +615,10 @@ __device__ __forceinline__ bool attn_latent_query(const LatArgs& A, int m, uint8
     if constexpr (EXACT) sweep(std::false_type{});
     sweep(std::true_type{});
 
-    // ---- epilogue: o_lat[h][m] = O / l, rounded to bf16.
-    const float inv = 1.0f / lane_pair_sum(l_run);
+    // ---- epilogue: o_lat[h][m] = O / l, rounded to bf16 (zeros for a query with no allowed key,
+    // whose l and O are both 0).
+    const float l_tot = lane_pair_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     uint16_t* dst = A.olat + ((size_t)h * M + m) * kLora + 4 * half;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt)

@@ -422,6 +422,18 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
                                             softmax_scale, static_cast<uint16_t*>(out), s));
 }
 
+int mla_check_topk(const int32_t* topk, int B, int T, int K, int64_t* counts, void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!counts) return MLA_E_NULL;
+    if (!aligned16(counts)) return MLA_E_ALIGN;
+    const Span ins[] = {{topk, (size_t)B * T * K * sizeof(int32_t)}};
+    const Span outs[] = {{counts, 4 * sizeof(int64_t)}};
+    if (any_alias(outs, 1, ins, 1)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    return launched(mla::launch_check_topk(topk, B, T, K, counts, static_cast<hipStream_t>(stream)));
+}
+
 int mla_selection_list_stride(int T, int K) {
     if (validate_topk(reinterpret_cast<const int32_t*>(16), 1, T, K) != MLA_OK) return 0;
     return mla::latent_list_stride(T, K);

@@ -36,6 +36,9 @@ hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B,
 // Selection bitmap [B][Wout][Tout] (Wout >= ceil(T/32), Tout >= T; the excess is zero-filled).
 hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout, int Tout,
                              uint32_t* bitmap, hipStream_t stream);
+// Counts of a selection's entries outside [-1, T), later than their query, repeated, and of
+// rows left with no allowed key (counts: device int64 [4], overwritten).
+hipError_t launch_check_topk(const int32_t* topk, int B, int T, int K, int64_t* counts, hipStream_t stream);
 // Bitmap geometry the attention kernel reads: words per query column and query columns.
 int attn_bitmap_words(int T);
 int attn_bitmap_cols(int T);

@@ -133,6 +133,21 @@ def test_attention_and_bitmap_validation():
     assert lib.mla_rope_table(8, -1.0, A, NOSTREAM) == -7
 
 
+def test_check_topk_validation():
+    lib = _lib()
+
+    def call(topk=D, B=1, T=64, K=16, counts=E):
+        return lib.mla_check_topk(topk, B, T, K, counts, NOSTREAM)
+    assert call(topk=None) == -1
+    assert call(counts=None) == -1
+    assert call(B=0) == -2
+    assert call(T=40000) == -2
+    assert call(K=0) == -2
+    assert call(topk=D + 4) == -3
+    assert call(counts=E + 8) == -3
+    assert call(counts=D + 16) == -8                  # counts inside the selection
+
+
 def test_latent_attention_and_lists_validation():
     lib = _lib()
     assert lib.mla_selection_list_stride(4096, 2048) == 2048

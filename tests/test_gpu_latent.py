@@ -1,16 +1,16 @@
-"""GPU parity of the latent-space attention (mla_sparse_prefill_attn_latent) and of the sorted
-selection lists it runs on, against the CPU oracle.
+"""GPU parity of the latent-space attention (mla_sparse_prefill_attn_latent), of the split form
+(mla_sparse_prefill_attn_auto) and of the sorted selection lists they run on, against the CPU
+oracle.
 
 The latent form regroups the pages' products (queries absorbed into the latent, values mixed in
-the latent), so its reference is the pages' form itself: oracle.kv_up of the latent rows followed
-by oracle.sparse_prefill_attn (or its per-row variant on sampled rows of the full workloads).
-Rounding differs from the pages' order only in where bf16 roundings sit (the absorbed query and
-the latent output instead of the per-head keys and values). Criteria: rel-L2 <= 1e-2 as for the
-head-major path, and per element |got - ref| <= 2e-2 + 2 bf16 steps of |ref|: the head-major
-allowance plus one step for each of the two extra roundings, each of which can move an output
-element by up to about one bf16 step of its own magnitude (the latent output is rounded once and
-then mixed by W_UV, so its error does not average out over keys the way the per-key value
-roundings of the pages' order do). The lists are integer work: bit-exact.
+the latent) and never forms the per-head keys and values, so it does not round them. Its
+reference is the pages' arithmetic with that rounding left out: oracle.kv_up(..., rounded=False)
+followed by oracle.sparse_prefill_attn, held to the attention bound (rel-L2 <= 1e-2 and max-abs
+<= 2e-2). The pages' order, which rounds the values of every head before mixing them, is also
+reported and held to rel-L2 <= 1e-2: by itself that rounding moves some outputs of few-key
+queries by one bf16 step of 2^-5 (a CPU pin shows it on exact arithmetic), which no regrouping
+can reproduce. Rows of the split form below the split take the head-major path and are held to
+the bound against the pages' order. The lists are integer work: bit-exact.
 """
 import numpy as np
 import pytest
@@ -30,16 +30,13 @@ SCALE = oracle.softmax_scale()
 f32 = synth.bf16_bits_to_f32
 
 
-def attention_close(got, ref, what=""):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = np.abs(got - ref)
-    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
-    excess = err - (2e-2 + 2 * bf16_step(ref))
-    say(f"  {what}: rel-L2 {rel:.3e}, max-abs {err.max():.3e}, worst margin {excess.max():.3e}")
-    assert rel <= 1e-2, f"{what}: rel-L2 {rel}"
-    assert (excess <= 0).all(), f"{what}: {(excess > 0).sum()} elements beyond 2e-2 + 2 bf16 steps"
+def latent_close(got, ref_exact, ref_pages, what=""):
+    """The attention bound against the unrounded form; rel-L2 against the pages' order."""
+    strict_attention_close(got, ref_exact, what)
+    d = np.asarray(got, np.float64) - ref_pages
+    rel = np.linalg.norm(d) / max(np.linalg.norm(ref_pages), 1e-30)
+    say(f"  {what} against the pages' rounded values: rel-L2 {rel:.3e}, max-abs {np.abs(d).max():.3e}")
+    assert rel <= 1e-2, f"{what}: rel-L2 against the pages' order {rel}"
 
 
 # ------------------------------------------------------------------------------------ lists
@@ -100,8 +97,11 @@ def _run_latent(q, c_kv, k_pe, w, topk):
 
 
 def _oracle(q, c_kv, k_pe, w, topk):
+    """(rounded kv, output of the pages' order, output without the kv rounding)."""
     kv = oracle.kv_up(f32(c_kv), f32(w))
-    return kv, oracle.sparse_prefill_attn(f32(q), kv, f32(k_pe), topk, SCALE)
+    kv_x = oracle.kv_up(f32(c_kv), f32(w), rounded=False)
+    return (kv, oracle.sparse_prefill_attn(f32(q), kv, f32(k_pe), topk, SCALE),
+            oracle.sparse_prefill_attn(f32(q), kv_x, f32(k_pe), topk, SCALE))
 
 
 # (1, 1100, 300): tiles of 32 keys with a ragged last tile for most rows; (1, 333, 400): K > T;
@@ -112,8 +112,8 @@ def test_latent_attention_matches_oracle(B, T, K):
     say(f"latent attention B={B} T={T} K={K}")
     q, c_kv, k_pe, w, topk = _latent_inputs(5000 + T + K, B, T, K)
     got = _run_latent(q, c_kv, k_pe, w, topk)
-    kv, ref = _oracle(q, c_kv, k_pe, w, topk)
-    attention_close(got, ref, f"latent B{B} T{T} K{K}")
+    kv, ref, ref_x = _oracle(q, c_kv, k_pe, w, topk)
+    latent_close(got, ref_x, ref, f"latent B{B} T{T} K{K}")
     # query 0 sees only key 0: the output is W_UV applied to that latent row, i.e. the value row
     # of the pages' form up to the fp32 summation order
     wv = f32(w).reshape(128, 256, 512)[:, 128:, :].astype(np.float64)
@@ -126,8 +126,8 @@ def test_latent_attention_full_selection_is_dense_causal():
     q, c_kv, k_pe, w, _ = _latent_inputs(5100, B, T, 1)
     topk = np.tile(np.arange(T, dtype=np.int32), (B, T, 1))
     got = _run_latent(q, c_kv, k_pe, w, topk)
-    _, ref = _oracle(q, c_kv, k_pe, w, topk)
-    attention_close(got, ref, "latent full selection")
+    _, ref, ref_x = _oracle(q, c_kv, k_pe, w, topk)
+    latent_close(got, ref_x, ref, "latent full selection")
 
 
 def test_latent_attention_exact_max_path():
@@ -139,21 +139,22 @@ def test_latent_attention_exact_max_path():
     kpe[0, 150] = 60.0                       # rotary part of key 150: scores of order +-60 per unit
     k_pe = synth.f32_to_bf16_bits(kpe)
     got = _run_latent(q, c_kv, k_pe, w, topk)
-    _, ref = _oracle(q, c_kv, k_pe, w, topk)
-    attention_close(got, ref, "latent exact-max path")
+    _, ref, ref_x = _oracle(q, c_kv, k_pe, w, topk)
+    latent_close(got, ref_x, ref, "latent exact-max path")
 
 
-def _latent_rows_ref(q, c_kv, k_pe, w, topk, b, rows):
+def _latent_rows_ref(q, c_kv, k_pe, w, topk, b, rows, rounded=False):
     """Oracle for sampled query rows of a large workload: each row's allowed keys alone, as a
     compact problem (the keys renumbered 0..n-1 in order, the query last). q: bf16 bits indexed
-    q[b, s] (an array, or any object with that indexing)."""
+    q[b, s] (an array, or any object with that indexing). ``rounded``: the pages' order (keys and
+    values rounded to bf16) instead of the unrounded form."""
     res = []
     wf = f32(w)
     for s in rows:
         ids = np.asarray(topk[b, s]).astype(np.int64)
         ids = np.unique(ids[(ids >= 0) & (ids <= s)])
         n = len(ids)
-        kv_c = oracle.kv_up(f32(c_kv[b:b + 1, ids]), wf)                     # [1, H, n, 256]
+        kv_c = oracle.kv_up(f32(c_kv[b:b + 1, ids]), wf, rounded=rounded)    # [1, H, n, 256]
         q_c = np.zeros((1, n, 128, 192), np.float32)
         q_c[0, n - 1] = f32(q[b, s])
         topk_c = np.full((1, n, n), -1, np.int32)
@@ -184,8 +185,9 @@ def test_latent_workload_sampled(name):
     for b in range(w.B):
         rows = sorted(set([0, 1, 31, 32, 33, K - 1, K, T - 1] + rng.integers(0, T, 4).tolist()))
         say(f"checking {len(rows)} sampled rows of batch {b}")
-        ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], b, rows)
-        attention_close(to_host(out[b, rows]), ref, f"{name} batch {b}")
+        ref_x = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], b, rows)
+        ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], b, rows, rounded=True)
+        latent_close(to_host(out[b, rows]), ref_x, ref, f"{name} batch {b}")
 
 
 # ------------------------------------------------------------------------------------ split form
@@ -200,8 +202,12 @@ def test_auto_attention_matches_oracle(B, T, K):
                                            torch.from_numpy(topk).to(dev()), SCALE)
     torch.cuda.synchronize()
     got = to_host(out)
-    _, ref = _oracle(q, c_kv, k_pe, w, topk)
-    attention_close(got, ref, f"split form B{B} T{T} K{K}")
+    _, ref, ref_x = _oracle(q, c_kv, k_pe, w, topk)
+    # rows below the split: head-major path on rounded keys and values; the rest: latent form
+    if split > 0:
+        strict_attention_close(got[:, :split], ref[:, :split], f"split form B{B} T{T} K{K}, head-major rows")
+    if split < T:
+        latent_close(got[:, split:], ref_x[:, split:], ref[:, split:], f"split form B{B} T{T} K{K}, latent rows")
 
 
 def test_auto_long_workload_sampled():
@@ -217,10 +223,13 @@ def test_auto_long_workload_sampled():
     assert 0 < split < w.T
     ckv_bits = c_kv.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     kpe_bits = k_pe.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    rows = [0, 1, split - 256, split - 1, split, split + 1, w.T - 1]
-    say(f"split {split}: checking rows {rows}")
-    ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], 0, rows)
-    attention_close(to_host(out[0, rows]), ref, "long split form")
+    lo, hi = [0, 1, split - 256, split - 1], [split, split + 1, w.T - 1]
+    say(f"split {split}: checking rows {lo + hi}")
+    got = to_host(out[0, lo + hi])
+    ref = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], 0, lo + hi, rounded=True)
+    ref_x = _latent_rows_ref(d["q"], ckv_bits, kpe_bits, d["w_ukv"], d["topk"], 0, hi)
+    strict_attention_close(got[:len(lo)], ref[:len(lo)], "long split form, head-major rows")
+    latent_close(got[len(lo):], ref_x, ref[len(lo):], "long split form, latent rows")
 
 
 class _Rows:
@@ -256,8 +265,12 @@ def test_longest_sequence_auto_and_head_major():
     rng = np.random.default_rng(4705)
     rows = sorted(set([0, 1, K - 1, split - 1, split, T - 2, T - 1] + rng.integers(0, T, 3).tolist()))
     qr = _Rows(q, rows)
-    ref = _latent_rows_ref(qr, ckv_bits, kpe_bits, w, topk, 0, rows)
-    attention_close(to_host(out[0, rows]), ref, "longest sequence, split form")
+    got = to_host(out[0, rows])
+    ref = _latent_rows_ref(qr, ckv_bits, kpe_bits, w, topk, 0, rows, rounded=True)
+    ref_x = _latent_rows_ref(qr, ckv_bits, kpe_bits, w, topk, 0, rows)
+    below = np.asarray(rows) < split
+    strict_attention_close(got[below], ref[below], "longest sequence, split form, head-major rows")
+    latent_close(got[~below], ref_x[~below], ref[~below], "longest sequence, split form, latent rows")
     say("  head-major path")
     kv = mla.mla_kv_up(c_kv, wu)
     out_hm = mla.mla_sparse_prefill_attn(q, kv, k_pe, tk, SCALE)

@@ -3,8 +3,8 @@ times (mla_kv_latent, mla_kv_up, mla_sparse_prefill_attn).
 
 The oracle checks sampled outputs (sampled token rows of the projections, sampled query rows of
 the attention, each from the GPU's own upstream tensors); the latent norm/rotary step and the
-selection bitmap are checked on every row. The 1k workload is small enough for the oracle to
-compute every output of the path.
+selection bitmap are checked on every row, and the headline attention on every output. The 1k
+workload is small enough for the oracle to compute every output of the path.
 """
 import numpy as np
 import pytest
@@ -96,6 +96,21 @@ def test_headline_workload_sampled():
         qrows = sorted(set([0, 1, 31, 32, K - 1, K, K + 1, T - 1] + rng.integers(0, T, 16).tolist()))
         say(f"checking attention rows of batch {b}")
         check_attention_rows(d, kv, k_pe, out, b, qrows)
+
+
+def test_headline_attention_every_output():
+    """Every output of the headline attention (both sequences, all 128 heads, every query row)
+    against the oracle's dense-masked form on the GPU's own keys, values and rotary keys: the
+    persistent kernel's pairing of query tiles and its per-XCD walk over heads is checked on all
+    of its work items."""
+    w = synth.WORKLOADS["headline"]
+    d, kv_raw, c_kv, k_pe, kv, out = run_path(w)
+    for b in range(w.B):
+        say(f"oracle on all of batch {b} ({w.T} queries x 128 heads)")
+        q = f32(d["q"][b:b + 1])
+        ref = oracle.sparse_prefill_attn(q, to_host(kv[b:b + 1]), to_host(k_pe[b:b + 1]),
+                                         d["topk"][b:b + 1], SCALE)
+        attention_close(to_host(out[b:b + 1]), ref, f"headline batch {b}, every output")
 
 
 def test_long_workload_sampled():

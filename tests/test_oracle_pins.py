@@ -313,30 +313,139 @@ def test_query_zero_and_self_only_selection_return_the_value_row():
     assert np.array_equal(out, kv[..., 128:].transpose(0, 2, 1, 3))
 
 
-def test_matches_the_pages_scatter_form_in_torch():
+def _sdpa_with_selection(q, kv, kpe, topk, scale):
+    """torch's scaled_dot_product_attention in float64 with a boolean mask built row by row from
+    each query's index set (Keys page, MHA-prefill excerpt: the index mask plus the causal mask,
+    shared by every head). Returns [B, T, H, 128] rounded to bf16 by torch's cast."""
+    B, T, H, _ = q.shape
+    allow = torch.zeros((B, 1, T, T), dtype=torch.bool)
+    for b in range(B):
+        for s in range(T):
+            for t in {int(e) for e in topk[b, s]}:
+                if 0 <= t <= s:
+                    allow[b, 0, s, t] = True
+    qt = torch.from_numpy(np.asarray(q, np.float64)).permute(0, 2, 1, 3)
+    kt = torch.cat([torch.from_numpy(np.asarray(kv[..., :128], np.float64)),
+                    torch.from_numpy(np.asarray(kpe, np.float64))[:, None].expand(B, H, T, 64)], -1)
+    vt = torch.from_numpy(np.asarray(kv[..., 128:], np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allow, scale=scale)
+    return o.permute(0, 2, 1, 3).float().to(torch.bfloat16).float().numpy()
+
+
+def test_matches_torch_sdpa_with_a_selection_mask():
+    """The selection with duplicates, -1 padding and future positions, as a boolean mask handed
+    to torch's attention routine."""
     B, T, H, K = 2, 16, 128, 6
     q, kv, kpe, topk = _tiny_attn_inputs(60, B, T, H, K)
+    topk[0, 9, :3] = [4, 4, 15]          # a repeated entry and a future position
+    topk[1, 3, 1:] = -1
     scale = oracle.softmax_scale()
     out = oracle.sparse_prefill_attn(q, kv, kpe, topk, scale)
-    # the pages' literal form: -inf mask, scatter 0 at the top-k positions, add causal mask,
-    # broadcast over heads, softmax, value einsum. Padding (-1) is replaced by the row's own
-    # position, which scatter then sets twice (set semantics).
-    s_idx = torch.arange(T)[None, :, None].expand(B, T, K)
-    idx = torch.from_numpy(topk).long()
-    idx = torch.where(idx < 0, s_idx, idx)
-    qt = torch.from_numpy(q).double()
-    k = torch.cat([torch.from_numpy(kv[..., :128]).double().permute(0, 2, 1, 3),
-                   torch.from_numpy(kpe).double()[:, :, None].expand(B, T, H, 64)], -1)
-    v = torch.from_numpy(kv[..., 128:]).double().permute(0, 2, 1, 3)
-    scores = torch.einsum("bshd,bthd->bsht", qt, k) * scale
-    index_mask = torch.full((B, T, T), float("-inf"), dtype=torch.float64).scatter_(-1, idx, 0)
-    causal = torch.full((T, T), float("-inf"), dtype=torch.float64).triu_(1)
-    index_mask += causal
-    scores += index_mask.unsqueeze(2)
-    ref = torch.einsum("bsht,bthd->bshd", scores.softmax(dim=-1), v)
-    ref = ref.float().to(torch.bfloat16).float().numpy()
+    ref = _sdpa_with_selection(q, kv, kpe, topk, scale)
     step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
     assert (np.abs(out - ref) <= step).all()
+
+
+def _torch_prefill(x, wd, gain, wu, q, topk, scale, eps=1e-6):
+    """The whole path composed from torch library routines only (linear, rms_norm, complex
+    multiply, attention), each stage consuming this function's own previous stage."""
+    bfr = lambda t: t.float().to(torch.bfloat16).float().double()
+    x, wd, wu = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wd, wu))
+    B, T, _ = x.shape
+    kv_raw = bfr(torch.nn.functional.linear(x, wd))
+    c, pe = kv_raw[..., :512], kv_raw[..., 512:]
+    c_kv = bfr(torch.nn.functional.rms_norm(c.float(), (512,), weight=torch.from_numpy(gain), eps=eps))
+    ang = torch.arange(T, dtype=torch.float64)[:, None] * 10000.0 ** (-torch.arange(0, 64, 2, dtype=torch.float64) / 64)
+    z = torch.view_as_complex(pe.reshape(B, T, 32, 2).contiguous()) * torch.polar(torch.ones_like(ang), ang)
+    k_pe = bfr(torch.view_as_real(z).reshape(B, T, 64))
+    kv = bfr(torch.nn.functional.linear(c_kv, wu)).reshape(B, T, 128, 256).permute(0, 2, 1, 3)
+    out = _sdpa_with_selection(q, kv.numpy(), k_pe.numpy(), topk, scale)
+    return {"kv_raw": kv_raw.numpy(), "c_kv": c_kv.numpy(), "k_pe": k_pe.numpy(), "kv": kv.numpy(), "out": out}
+
+
+def test_mla_prefill_matches_an_independent_torch_composition():
+    """oracle.mla_prefill end to end from x (the down-projection page's key-value excerpt, then
+    the Keys page's MHA-prefill excerpt) against the same steps written with torch routines."""
+    B, T, K = 2, 12, 5
+    x = bf(100, (B, T, 7168))
+    wd = bf(101, (576, 7168), 7168 ** -0.5)
+    wu = bf(102, (32768, 512), 512 ** -0.5)
+    gain = (1.0 + bf(103, (512,), 0.1 ** 0.5)).astype(np.float32)
+    gain = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(gain))
+    q = bf(104, (B, T, 128, 192))
+    topk = synth.random_topk(105, B, T, K)
+    scale = oracle.softmax_scale()
+    got = oracle.mla_prefill(x, wd, gain, wu, q, topk, scale)
+    ref = _torch_prefill(x, wd, gain, wu, q, topk, scale)
+    for name in ("kv_raw", "c_kv", "k_pe", "kv"):
+        r = ref[name]
+        step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+        assert (np.abs(got[name] - r) <= step).all(), name
+    d = got["out"] - ref["out"]
+    assert np.linalg.norm(d) <= 1e-3 * np.linalg.norm(ref["out"])
+    assert np.abs(d).max() <= 2e-2
+    # the composition tells the inputs apart: swapping the two weights' roles is impossible by
+    # shape, but a path without the norm, or with the rotary key left unrotated, is not this one
+    no_norm = oracle.sparse_prefill_attn(q, oracle.kv_up(got["kv_raw"][..., :512], wu),
+                                         got["k_pe"], topk, scale)
+    assert np.abs(no_norm - ref["out"]).max() > 0.1
+    unrotated = oracle.sparse_prefill_attn(q, got["kv"], got["kv_raw"][..., 512:], topk, scale)
+    assert np.abs(unrotated - ref["out"]).max() > 0.1
+
+
+def test_regrouped_products_equal_the_unrounded_form():
+    """Associativity: scoring the latent rows with the absorbed query W_UK^T q_nope, mixing the
+    latent rows and mapping the mix through W_UV gives the pages' attention computed without
+    the bf16 rounding of the per-head keys and values (``kv_up(..., rounded=False)``)."""
+    B, T, K = 1, 20, 6
+    q = bf(110, (B, T, 128, 192))
+    c = bf(111, (B, T, 512))
+    kpe = bf(112, (B, T, 64))
+    wu = bf(113, (32768, 512), 512 ** -0.5)
+    topk = synth.random_topk(114, B, T, K)
+    scale = oracle.softmax_scale()
+    out = oracle.sparse_prefill_attn(q, oracle.kv_up(c, wu, rounded=False), kpe, topk, scale)
+    W = torch.from_numpy(wu.astype(np.float64)).reshape(128, 256, 512)
+    wuk, wuv = W[:, :128], W[:, 128:]                       # [h, 128, 512]
+    qt = torch.from_numpy(q.astype(np.float64))[0]         # [T, h, 192]
+    ct = torch.from_numpy(c.astype(np.float64))[0]         # [T, 512]
+    pt = torch.from_numpy(kpe.astype(np.float64))[0]       # [T, 64]
+    ref = np.zeros((T, 128, 128))
+    for s in range(T):
+        ids = sorted({int(e) for e in topk[0, s] if 0 <= e <= s})
+        q_lat = torch.bmm(qt[s, :, None, :128], wuk)[:, 0]                      # [h, 512]
+        sc = scale * (q_lat @ ct[ids].T + qt[s, :, 128:] @ pt[ids].T)           # [h, n]
+        o_lat = torch.softmax(sc, -1) @ ct[ids]                                 # [h, 512]
+        ref[s] = torch.bmm(wuv, o_lat[:, :, None])[:, :, 0].numpy()
+    ref = oracle.bf16(ref)
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert (np.abs(out[0] - ref) <= step).all()
+
+
+def test_rounding_of_the_per_head_values_alone_exceeds_the_attention_bound():
+    """The pages' order rounds every head's values to bf16 before mixing them. For queries with
+    few keys the output has the magnitude of single value rows, where one bf16 step is 2^-5
+    (|out| >= 4): the unrounded form and the rounded form then differ by more than 2e-2 in some
+    elements, while their rel-L2 distance stays far below 1e-2. A regrouped computation, which
+    never forms the values, is therefore held to the attention bound against the unrounded
+    form."""
+    B, T, K = 3, 130, 7
+    seed = 5137
+    q = synth.bf16_bits_to_f32(synth.random_bf16(seed, (B, T, 128, 192)))
+    c = synth.bf16_bits_to_f32(synth.random_bf16(seed + 1, (B, T, 512)))
+    kpe = synth.bf16_bits_to_f32(synth.random_bf16(seed + 2, (B, T, 64)))
+    wu = synth.bf16_bits_to_f32(synth.random_bf16(seed + 3, (32768, 512), 512 ** -0.5))
+    topk = synth.random_topk(seed + 4, B, T, K)
+    scale = oracle.softmax_scale()
+    rounded = oracle.sparse_prefill_attn(q, oracle.kv_up(c, wu), kpe, topk, scale)
+    exact = oracle.sparse_prefill_attn(q, oracle.kv_up(c, wu, rounded=False), kpe, topk, scale)
+    d = np.abs(rounded.astype(np.float64) - exact)
+    assert d.max() > 2e-2
+    assert np.linalg.norm(rounded - exact) <= 5e-3 * np.linalg.norm(exact)
+    # every difference is the values' rounding carried through the weights: at most one bf16
+    # step of the largest value row involved plus one output rounding
+    vmax = np.abs(oracle.kv_up(c, wu)[..., 128:]).max()
+    assert d.max() <= 2.0 ** (np.floor(np.log2(vmax)) - 7) + 2.0 ** (np.floor(np.log2(np.abs(exact).max())) - 7)
 
 
 def test_pure_python_brute_force_tiny():
@@ -396,3 +505,33 @@ def test_empty_allowed_set_is_rejected():
     topk[0, 2, 0] = 3            # row 2 selects only a future key
     with pytest.raises(ValueError):
         oracle.sparse_prefill_attn(q, kv, kpe, topk, 0.1)
+
+
+def test_topk_defects_brute_force():
+    """Counts of out-of-range, future and repeated entries and of empty rows, against a plain
+    loop over every row's entries with a Python set."""
+    rng = np.random.default_rng(7)
+    B, T, K = 2, 23, 9
+    topk = rng.integers(-4, T + 4, (B, T, K)).astype(np.int32)
+    topk[0, 5] = -1                      # an all-padding row
+    topk[1, 0] = [3, 7, 22, -1, -1, -1, 30, 1, 2]   # query 0 with only later positions
+    topk[1, 9, :4] = [2, 2, 2, 9]
+    want = {"invalid": 0, "future": 0, "repeated": 0, "empty_rows": 0}
+    for b in range(B):
+        for s in range(T):
+            seen = set()
+            for e in topk[b, s]:
+                e = int(e)
+                if e < -1 or e >= T:
+                    want["invalid"] += 1
+                elif e > s:
+                    want["future"] += 1
+                elif e >= 0:
+                    if e in seen:
+                        want["repeated"] += 1
+                    seen.add(e)
+            want["empty_rows"] += not seen
+    assert oracle.topk_defects(topk, T) == want
+    assert want["empty_rows"] >= 2 and want["repeated"] >= 2
+    clean = synth.random_topk(8, 1, 40, 12)
+    assert oracle.topk_defects(clean, 40) == {"invalid": 0, "future": 0, "repeated": 0, "empty_rows": 0}
