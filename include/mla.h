@@ -72,8 +72,12 @@ enum {
     MLA_E_DEVICE = -5,     /* current device is not gfx950, or no device */
     MLA_E_LAUNCH = -6,     /* a kernel launch failed (see mla_last_hip_error) */
     MLA_E_ARG = -7,        /* eps, theta or softmax_scale not finite and > 0 */
-    MLA_E_ALIAS = -8       /* an output overlaps an input or another output */
+    MLA_E_ALIAS = -8,      /* an output overlaps an input or another output */
+    MLA_E_SCRATCH = -9     /* beyond the fixed scratch of mla_sparse_prefill_attn_noalloc */
 };
+
+/* Bytes of device scratch mla_sparse_prefill_attn_noalloc holds on each device it runs on. */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Joint KV down-projection, latent RMSNorm and rotary key (one call for the front end).
@@ -311,6 +315,29 @@ int mla_attn_prepare(const int32_t* topk, int B, int T, int K, void* workspace, 
 int mla_sparse_prefill_attn_prepared(const void* q, const void* kv, const void* k_pe, int B, int T,
                                      float softmax_scale, void* out, const void* workspace,
                                      size_t ws_bytes, void* stream);
+
+/*
+ * mla_sparse_prefill_attn for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and result,
+ * with the selection bitmap kept in a fixed device array of MLA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device for the life of the process, instead of a caller workspace. The
+ * call allocates nothing (no hipMalloc, no library allocation) and only enqueues work.
+ *   q, kv, k_pe, topk, B, T, K, softmax_scale, out   as for mla_sparse_prefill_attn.
+ * Limit: the bitmap, mla_noalloc_scratch_bytes(B, T) = 4 * B * (2 * ceil(T/64)) * (256 * ceil(T/256))
+ * bytes, must fit the scratch (B * T^2 / 8 <= 32 MiB for T a multiple of 256: B <= 16 at T = 4096,
+ * B = 1 at T = 16384); larger problems are rejected with MLA_E_SCRATCH before anything is enqueued.
+ * Every call on one device shares that device's scratch: calls that may overlap on one device
+ * (different streams, or different threads without ordering) race, and must be serialised by the
+ * caller. The scratch keeps the last call's bitmap; nothing in it has to start at zero.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_ARG, MLA_E_ALIAS, MLA_E_SCRATCH, MLA_E_DEVICE,
+ *         MLA_E_LAUNCH.
+ */
+int mla_sparse_prefill_attn_noalloc(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
+                                    int B, int T, int K, float softmax_scale, void* out, void* stream);
+
+/* Scratch bytes mla_sparse_prefill_attn_noalloc needs for B sequences of length T (0 for shapes the
+ * attention calls reject). */
+size_t mla_noalloc_scratch_bytes(int B, int T);
 
 /*
  * Row stride (entries) of the selection lists: ceil(min(T, K) / 64) * 64. Returns 0 for shapes the

@@ -41,6 +41,8 @@ _SIGS = {
     "mla_attn_prepare": (_I, [_VP, _I, _I, _I, _VP, _SZ, _VP]),
     "mla_sparse_prefill_attn_prepared": (_I, [_VP, _VP, _VP, _I, _I, _F, _VP, _VP, _SZ, _VP]),
     "mla_check_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "mla_sparse_prefill_attn_noalloc": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _F, _VP, _VP]),
+    "mla_noalloc_scratch_bytes": (_SZ, [_I, _I]),
     "mla_selection_list_stride": (_I, [_I, _I]),
     "mla_selection_lists": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "mla_attn_latent_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -431,6 +433,38 @@ def mla_sparse_prefill_attn(q, kv, k_pe, topk, softmax_scale: float | None = Non
                                              softmax_scale, _ptr(out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(),
                                              _stream(q.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def mla_noalloc_scratch_bytes(B: int, T: int) -> int:
+    return int(lib().mla_noalloc_scratch_bytes(B, T))
+
+
+def mla_sparse_prefill_attn_noalloc(q, kv, k_pe, topk, softmax_scale: float | None = None, out=None):
+    """mla_sparse_prefill_attn without a workspace: the library's fixed per-device scratch holds
+    the selection bitmap (at most NOALLOC_SCRATCH_BYTES). Pass `out` to avoid any allocation here
+    as well. Calls that overlap on one device race on the scratch."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, 128, 192]")
+    B, T = q.shape[0], q.shape[1]
+    _need(q, "q", torch.bfloat16, (B, T, HEADS, QK_HEAD))
+    _need(kv, "kv", torch.bfloat16, (B, HEADS, T, QK_NOPE + V_HEAD))
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, ROPE))
+    if topk.dim() != 3 or topk.shape[:2] != (B, T):
+        raise ValueError("topk must be [B, T, K]")
+    _need(topk, "topk", torch.int32)
+    K = topk.shape[2]
+    if softmax_scale is None:
+        softmax_scale = mla_default_softmax_scale()
+    if out is None:
+        out = torch.empty((B, T, HEADS, V_HEAD), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, HEADS, V_HEAD))
+    with torch.cuda.device(q.device):
+        _check(lib().mla_sparse_prefill_attn_noalloc(_ptr(q), _ptr(kv), _ptr(k_pe), _ptr(topk), B, T, K,
+                                                     softmax_scale, _ptr(out), _stream(q.device)))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/mla.h"
 #include "mla_launch.hpp"
@@ -148,6 +149,32 @@ size_t attn_bitmap_bytes(int B, int T) {
 }
 // Bitmap as mla_selection_bitmap returns it, [B][ceil(T/32)][T].
 size_t plain_bitmap_bytes(int B, int T) { return (size_t)B * ((T + 31) / 32) * T * sizeof(uint32_t); }
+
+// Scratch of mla_sparse_prefill_attn_noalloc: the selection bitmap lives in this fixed array
+// instead of a caller workspace. Each device holds its own copy for the life of the process. In
+// host code `scratch` names a host-side stand-in, not the device copy: the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// Device address of this device's scratch (the current device), or nullptr on failure.
+void* scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_hip_error = (int)e;
+            return nullptr;
+        }
+        g_scratch_dev[dev] = p;
+    }
+    return g_scratch_dev[dev];
+}
 
 }  // namespace
 
@@ -434,6 +461,43 @@ int mla_check_topk(const int32_t* topk, int B, int T, int K, int64_t* counts, vo
     return launched(mla::launch_check_topk(topk, B, T, K, counts, static_cast<hipStream_t>(stream)));
 }
 
+int mla_sparse_prefill_attn_noalloc(const void* q, const void* kv, const void* k_pe, const int32_t* topk,
+                                    int B, int T, int K, float softmax_scale, void* out, void* stream) {
+    int st = validate_topk(topk, B, T, K);
+    if (st != MLA_OK) return st;
+    if (!q || !kv || !k_pe || !out) return MLA_E_NULL;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(k_pe) || !aligned16(out)) return MLA_E_ALIGN;
+    if (!pos_finite(softmax_scale)) return MLA_E_ARG;
+    if (attn_bitmap_bytes(B, T) > kScratchBytes) return MLA_E_SCRATCH;
+    const size_t M = (size_t)B * T;
+    const Span ins[] = {{q, M * MLA_HEADS * MLA_QK_HEAD * kBf16},
+                        {kv, M * MLA_HEADS * 256 * kBf16},
+                        {k_pe, M * MLA_ROPE * kBf16},
+                        {topk, M * K * sizeof(int32_t)}};
+    const Span outs[] = {{out, M * MLA_HEADS * MLA_V_HEAD * kBf16}};
+    if (any_alias(outs, 1, ins, 4)) return MLA_E_ALIAS;
+    if ((st = check_device()) != MLA_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_E_DEVICE;
+    uint32_t* bm = static_cast<uint32_t*>(scratch_address(dev));
+    if (!bm) return MLA_E_DEVICE;
+    // every word of the bitmap region the attention reads is written by the bitmap kernel
+    // (zeros past the sequence), so the scratch needs no clearing between calls
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
+                                         mla::attn_bitmap_cols(T), bm, s));
+    if (st != MLA_OK) return st;
+    return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
+                                            static_cast<const uint16_t*>(kv),
+                                            static_cast<const uint16_t*>(k_pe), bm, B, T,
+                                            softmax_scale, static_cast<uint16_t*>(out), s));
+}
+
+size_t mla_noalloc_scratch_bytes(int B, int T) {
+    if (validate_topk(reinterpret_cast<const int32_t*>(16), B, T, 1) != MLA_OK) return 0;
+    return attn_bitmap_bytes(B, T);
+}
+
 int mla_selection_list_stride(int T, int K) {
     if (validate_topk(reinterpret_cast<const int32_t*>(16), 1, T, K) != MLA_OK) return 0;
     return mla::latent_list_stride(T, K);
@@ -539,6 +603,8 @@ const char* mla_status_string(int status) {
         case MLA_E_LAUNCH: return "MLA_E_LAUNCH: kernel launch failed";
         case MLA_E_ARG: return "MLA_E_ARG: eps/theta/scale must be finite and positive";
         case MLA_E_ALIAS: return "MLA_E_ALIAS: an output overlaps another buffer";
+        case MLA_E_SCRATCH:
+            return "MLA_E_SCRATCH: the problem needs more than the fixed scratch of the no-allocation entry point";
         default: return "unknown status";
     }
 }

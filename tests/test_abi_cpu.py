@@ -44,7 +44,7 @@ def test_host_only_helpers():
     m = 1 + 0.1 * math.log(40)
     assert s == pytest.approx(m * m / math.sqrt(192), rel=1e-7)
     assert lib.mla_status_string(0) == b"MLA_OK"
-    for code in range(-8, 0):
+    for code in range(-9, 0):
         assert lib.mla_status_string(code).startswith(b"MLA_E_")
     assert b"gfx950" in lib.mla_build_info()
     # bitmap words: B * (2 * ceil(T/64)) words x (256 * ceil(T/256)) query columns x 4 bytes
@@ -146,6 +146,28 @@ def test_check_topk_validation():
     assert call(topk=D + 4) == -3
     assert call(counts=E + 8) == -3
     assert call(counts=D + 16) == -8                  # counts inside the selection
+
+
+def test_noalloc_attention_validation():
+    lib = _lib()
+    assert mla.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert lib.mla_noalloc_scratch_bytes(2, 4096) == lib.mla_attn_workspace_bytes(2, 4096, 2048)
+    assert lib.mla_noalloc_scratch_bytes(1, 16384) == 32 << 20
+    assert lib.mla_noalloc_scratch_bytes(0, 64) == 0
+
+    def call(q=A, kv=B_, kpe=C, topk=D, B=1, T=64, K=16, scale=0.135, out=E):
+        return lib.mla_sparse_prefill_attn_noalloc(q, kv, kpe, topk, B, T, K, scale, out, NOSTREAM)
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(K=0) == -2
+    assert call(T=40000) == -2
+    assert call(out=E + 4) == -3
+    assert call(scale=-1.0) == -7
+    assert call(out=A + 64) == -8
+    assert call(T=32768) == -9                        # bitmap of 128 MiB: beyond the scratch
+    assert call(B=17, T=4096) == -9                   # 34 MiB
+    assert call(B=16, T=4096, out=A + 64) == -8       # 32 MiB fits; then the alias check
+    assert lib.mla_status_string(-9).startswith(b"MLA_E_SCRATCH")
 
 
 def test_latent_attention_and_lists_validation():
