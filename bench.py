@@ -71,36 +71,154 @@ def traffic_record(kernel: str):
     return float(kv["bytes_per_launch"])
 
 
-def cpu_baseline(d: dict, B: int, T: int, heads_sample: int) -> dict:
-    """Time the CPU oracle on batch 0: the front end and up-projection for all of its tokens,
-    the attention for `heads_sample` of its 128 heads; scale linearly to the whole workload."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name() -> str:
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:   # noqa: BLE001
+        return "unknown"
+
+
+_POOL_STATE = {}
+
+
+def _attn_heads(heads):
+    """Worker: the oracle's attention for some heads (inputs inherited at fork)."""
+    import oracle
+    st = _POOL_STATE
+    oracle.sparse_prefill_attn(st["q"], st["kv"], st["k_pe"], st["topk"], st["scale"], heads=heads)
+    return len(heads)
+
+
+def cpu_baseline_child(workload: str) -> dict:
+    """The CPU oracle timed on the host cores (runs in a child process that never touches the GPU).
+
+    The whole workload: its front end and up-projection for all tokens with BLAS on every core of
+    the affinity mask, then the dense-masked attention of all 128 heads over a process pool (one
+    worker per core of the mask, at most 16, one BLAS thread each, heads dealt round-robin). Then
+    the tiny and 1k workloads end to end on one core (one process, one BLAS thread)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:   # noqa: BLE001
-        cores = 1
     f32 = synth.bf16_bits_to_f32
-    x = f32(d["x"][:1])
-    t0 = time.perf_counter()
-    kv_raw, c_kv, k_pe = oracle.kv_latent(x, f32(d["w_dkv"]), d["gain"])
-    t1 = time.perf_counter()
-    kv = oracle.kv_up(c_kv, f32(d["w_ukv"]))
-    t2 = time.perf_counter()
-    q = f32(d["q"][:1])
-    oracle.sparse_prefill_attn(q, kv, k_pe, d["topk"][:1], oracle.softmax_scale(),
-                               heads=range(heads_sample))
-    t3 = time.perf_counter()
-    per_batch = (t1 - t0) + (t2 - t1) + (t3 - t2) * (128 / heads_sample)
-    total = per_batch * B
-    return {"value": B * T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"batch 0 of {B}: front end + up-projection for all {T} tokens "
-                       f"({t1 - t0:.1f} s + {t2 - t1:.1f} s), dense-masked attention for "
-                       f"{heads_sample} of 128 heads ({t3 - t2:.1f} s); scaled linearly to "
-                       f"{B} batches x 128 heads. float64 NumPy; BLAS threads = cores, "
-                       f"elementwise single-threaded"),
-            "sample_seconds": round(t3 - t0, 2)}
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, cores))
+    w = synth.WORKLOADS[workload]
+    d = synth.make(w)
+    B, T = w.B, w.T
+    scale = oracle.softmax_scale()
+    with threadpool_limits(cores):
+        t0 = time.perf_counter()
+        kv_raw, c_kv, k_pe = oracle.kv_latent(f32(d["x"]), f32(d["w_dkv"]), d["gain"])
+        t1 = time.perf_counter()
+        kv = oracle.kv_up(c_kv, f32(d["w_ukv"]))
+        t2 = time.perf_counter()
+    _POOL_STATE.update(q=f32(d["q"]), kv=kv, k_pe=k_pe, topk=d["topk"], scale=scale)
+    chunks = [list(range(i, 128, workers)) for i in range(workers)]
+    ctx = mp.get_context("fork")
+    with threadpool_limits(1):
+        t3 = time.perf_counter()
+        with ctx.Pool(workers) as pool:
+            assert sum(pool.map(_attn_heads, chunks)) == 128
+        t4 = time.perf_counter()
+    total = (t1 - t0) + (t2 - t1) + (t4 - t3)
+    one_core = {}
+    with threadpool_limits(1):
+        for name in ("tiny", "1k"):
+            wl = synth.WORKLOADS[name]
+            dd = synth.make(wl)
+            s0 = time.perf_counter()
+            oracle.mla_prefill(f32(dd["x"]), f32(dd["w_dkv"]), dd["gain"], f32(dd["w_ukv"]), f32(dd["q"]),
+                               dd["topk"], scale)
+            sec = time.perf_counter() - s0
+            one_core[name] = {"tokens_per_s": wl.B * wl.T / sec, "seconds": round(sec, 2)}
+    return {"value": B * T / total, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": (f"the whole workload ({B} x {T} tokens): front end + up-projection "
+                       f"({t1 - t0:.1f} s + {t2 - t1:.1f} s, BLAS on {cores} cores), dense-masked "
+                       f"attention of all 128 heads ({t4 - t3:.1f} s, {workers} worker processes x 1 "
+                       f"BLAS thread); float64 NumPy"),
+            "sample_seconds": round(t4 - t0, 2), "affinity_cores": cores, "cpu_model": _cpu_model(),
+            "blas": _blas_name(), "one_core_end_to_end": one_core}
+
+
+def cpu_baseline(workload: str) -> dict:
+    """Run cpu_baseline_child in a fresh interpreter (a child process: this one holds the GPU)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--workload", workload],
+                       capture_output=True, text=True, timeout=900)
+    if r.returncode != 0:
+        return {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle",
+                "sample": f"failed: {r.stderr[-500:]}"}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def executed_mfma_flop(B: int, T: int) -> float:
+    """MFMA work sparse_attn_kernel executes on its tile schedule: per (b, h) and query tile of 256
+    (q0 = 256 qt), each of the 8 waves runs 24 score MFMAs on tile 0, then 24 + 16 per key tile for
+    the nkt = (min(T, q0 + 256) - 1) // 64 + 1 key tiles up to the tile's last query (the last
+    iteration also scores one tile past the end, discarded), at 2 * 32 * 32 * 16 FLOP each."""
+    per_bh = 0
+    for qt in range((T + 255) // 256):
+        nkt = (min(T, 256 * qt + 256) - 1) // 64 + 1
+        per_bh += 8 * (24 + 40 * nkt)
+    return float(per_bh) * B * 128 * 2 * 32 * 32 * 16
+
+
+def sample_gfx_clock(torch, fn, reps: int) -> float | None:
+    """Median GFX clock (MHz) read through amdsmi while fn() runs `reps` times, or None."""
+    try:
+        import threading
+
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:   # noqa: BLE001
+        return None
+    vals, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                c = m.get("current_gfxclks") or m.get("current_gfxclk")
+                if isinstance(c, (list, tuple)):
+                    c = [x for x in c if isinstance(x, (int, float)) and 0 < x < 10000]
+                    c = sum(c) / len(c) if c else None
+                if isinstance(c, (int, float)) and 400 < c < 10000:   # below the 500 MHz floor: idle
+                    vals.append(float(c))
+            except Exception:   # noqa: BLE001
+                pass
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    th.start()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:   # noqa: BLE001
+        pass
+    return float(np.median(vals)) if vals else None
 
 
 def timed_us(torch, stream, fn, reps: int = 20, warm: int = 5) -> float:
@@ -227,12 +345,16 @@ def main():
                          "mla_sparse_prefill_attn_latent (no per-head keys and values); auto: "
                          "mla_sparse_prefill_attn_auto (head-major below the split row, latent above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time the CPU oracle only and print its JSON record (used as a child process)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 256 MiB fill and copy so a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE against known byte counts")
     args = ap.parse_args()
 
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline_child(args.workload)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU runs are not supported by this build", file=sys.stderr)
@@ -320,6 +442,11 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     side = side_measurements(torch, mla, dev, stream, topk, B, T, K)
+    clock_mhz = None
+    if kv is not None:
+        stream.wait_event(sync_ready)
+        clock_mhz = sample_gfx_clock(torch, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale,
+                                                                                         out=out), 400)
 
     if args.copy_calibration:
         src = torch.ones(1 << 26, dtype=torch.int32, device=dev)      # writes 256 MiB
@@ -330,6 +457,7 @@ def main():
 
     pairs = selected_pairs(d["topk"])
     attn_flop = 640.0 * pairs * 128
+    exec_flop = executed_mfma_flop(B, T) if kv is not None else None
     causal_pairs = B * T * (T + 1) // 2
     achieved = attn_flop / (att * 1e-3) / 1e12
     flop_down = 2.0 * B * T * 7168 * 576
@@ -367,7 +495,13 @@ def main():
                                 "sparse_attn kernel (mla_sparse_prefill_attn_prepared; the selection "
                                 "bitmap is built by mla_attn_prepare on a second stream during the "
                                 "projections)"),
-                     "algorithmic_flop_per_launch": attn_flop},
+                     "algorithmic_flop_per_launch": attn_flop,
+                     "executed_mfma_flop_per_launch": exec_flop,
+                     "executed_over_algorithmic": None if exec_flop is None else exec_flop / attn_flop,
+                     "measured_gfx_clock_mhz": clock_mhz,
+                     "peak_at_measured_clock": None if clock_mhz is None else PEAK_BF16_TFLOPS * clock_mhz / 2400.0,
+                     "frac_at_measured_clock": (None if clock_mhz is None else
+                                                achieved / (PEAK_BF16_TFLOPS * clock_mhz / 2400.0))},
         "stages_ms": {"kv_latent": lat, "kv_up": upm, "sparse_attn": att, "gpu_step": gpu_step},
         "stage_tflops": {"kv_latent": flop_down / (lat * 1e-3) / 1e12,
                          "kv_up": None if kv is None else flop_up / (upm * 1e-3) / 1e12},
@@ -376,11 +510,11 @@ def main():
         "bandwidth_kernels": side,
         "selected_pairs_all_batches": pairs,
         "latent_mfma_flop_per_launch": (2176.0 * pairs * 128 + 2 * 2.0 * tokens * 128 * 128 * 512) if latent else None,
-        "scored_over_selected_upper_bound": causal_pairs / pairs,
+        "causal_over_selected": causal_pairs / pairs,
         "input_generation_s": round(t_gen, 2),
     }
     if rank == 0 and not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(d, B, T, min(args.cpu_heads, 128))
+        res["cpu_baseline"] = cpu_baseline(args.workload)
     if rank == 0:
         print(json.dumps(res), flush=True)
 

@@ -26,7 +26,11 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    # every warning is an error, except the one clang gives for naming m0 in the clobber list of
+    # the global->LDS load helpers (mla_device.hpp): m0 is a reserved register, and the generated
+    # code of every kernel writes and reads m0 only inside those helpers, so no value of the
+    # compiler's own lives in m0 across them
+    "-Wall", "-Wextra", "-Werror", "-Wno-inline-asm", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 #pragma unroll
         for (int i = 0; i < 24; ++i) {
             const int j = i >> 1, blk = i & 1;
-            bf16x8 nx;
+            bf16x8 nx = r2;   // unused past the last step
             if (i + 3 < 24) nx = rd((i + 3) >> 1, (i + 3) & 1);
             s[blk] = mfma32x32x16(r0, qf[j], s[blk]);
             r0 = r1;

@@ -1,5 +1,5 @@
-// Query RMSNorm of the query path (the two GEMMs around it are the down-projection kernel's
-// template in gemm.hip).
+// Query RMSNorm of the query path (the two GEMMs around it are gemm_big_kernel in
+// gemm_big.hip).
 //
 // "DeepSeek V4.1 · Key-value RMSNorm" (formula and RMSNorm excerpt): per row, the fp32 mean of
 // squares, y = gain * x * rsqrt(mean + eps), cast back to bf16; "DeepSeek-V3.2-Exp · Key-value

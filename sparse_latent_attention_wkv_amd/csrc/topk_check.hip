@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void check_topk_kernel(const int32_t* __restri
     }
     __syncthreads();
     unsigned int empty = 0;
-    if (threadIdx.x < nrows && distinct[threadIdx.x] == 0) empty = 1;
+    if ((int)threadIdx.x < nrows && distinct[threadIdx.x] == 0) empty = 1;
     // wave sums, one atomic per wave and counter
     auto wsum = [](unsigned int v) {
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

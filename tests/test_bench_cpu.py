@@ -32,3 +32,16 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_executed_mfma_work_matches_the_counted_instructions():
+    """The schedule formula behind executed_mfma_flop_per_launch against the MFMA instruction
+    count rocprofv3 recorded for the headline launch (profiles/sparse_attn_traffic.txt)."""
+    flop = bench.executed_mfma_flop(2, 4096)
+    assert flop / (2 * 32 * 32 * 16) == 45350912
+    rec = open(os.path.join(ROOT, "profiles", "sparse_attn_traffic.txt")).read()
+    counted = float(rec.split("per dispatch: SQ_INSTS_MFMA ")[1].split(",")[0])
+    assert abs(flop / (2 * 32 * 32 * 16) - counted) <= 5e-5 * counted
+    # tiny shapes: one query tile, nkt = ceil(T / 64) key tiles, 8 waves
+    assert bench.executed_mfma_flop(1, 64) == 128 * 8 * (24 + 40) * 32768
+    assert bench.executed_mfma_flop(1, 65) == 128 * 8 * (24 + 80) * 32768
