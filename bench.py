@@ -347,6 +347,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="time the CPU oracle only and print its JSON record (used as a child process)")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="skip the engine-clock sampling (profiler runs)")
+    ap.add_argument("--side-only", action="store_true",
+                    help="run only the measurements outside the step (bandwidth-bound kernels, query path) "
+                         "and print them; a profiler run of this mode sees each of those kernels alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 256 MiB fill and copy so a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE against known byte counts")
@@ -425,6 +430,15 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    if args.side_only:
+        print(json.dumps({"bandwidth_kernels": side_measurements(torch, mla, dev, stream, topk, B, T, K)}),
+              flush=True)
+        return
+    # The measurements outside the step run first: on a GPU that was idle, the first milliseconds
+    # of load run at a lower engine clock (the attention's first launches take up to 30% longer),
+    # and the timed steps are meant to show the steady state.
+    side_meas = side_measurements(torch, mla, dev, stream, topk, B, T, K)
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -441,9 +455,8 @@ def main():
     gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
 
-    side = side_measurements(torch, mla, dev, stream, topk, B, T, K)
     clock_mhz = None
-    if kv is not None:
+    if kv is not None and not args.no_clock_sample:
         stream.wait_event(sync_ready)
         clock_mhz = sample_gfx_clock(torch, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale,
                                                                                          out=out), 400)
@@ -507,7 +520,7 @@ def main():
                          "kv_up": None if kv is None else flop_up / (upm * 1e-3) / 1e12},
         "attention_only_tokens_per_s": tokens / (att * 1e-3),
         "attention_mfma_busy_frac": mfma_busy_record() if headline else None,
-        "bandwidth_kernels": side,
+        "bandwidth_kernels": side_meas,
         "selected_pairs_all_batches": pairs,
         "latent_mfma_flop_per_launch": (2176.0 * pairs * 128 + 2 * 2.0 * tokens * 128 * 128 * 512) if latent else None,
         "causal_over_selected": causal_pairs / pairs,
