@@ -166,16 +166,58 @@ def cpu_baseline(workload: str) -> dict:
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-def executed_mfma_flop(B: int, T: int) -> float:
+def flagged_tiles(topk: np.ndarray) -> np.ndarray:
+    """Key tiles the attention kernel scores per (b, 256-query tile): the 64-key tiles holding an
+    allowed key (a valid entry at or before its query) of some query of the tile; at least one."""
+    B, T, K = topk.shape
+    nqt = (T + 255) // 256
+    n = np.zeros((B, nqt), np.int64)
+    for b in range(B):
+        for qt in range(nqt):
+            rows = topk[b, 256 * qt:256 * qt + 256].astype(np.int64)
+            s = np.arange(256 * qt, 256 * qt + len(rows))[:, None]
+            n[b, qt] = max(1, len(np.unique(rows[(rows >= 0) & (rows < T) & (rows <= s)] // 64)))
+    return n
+
+
+def executed_mfma_flop(tiles: np.ndarray) -> float:
     """MFMA work sparse_attn_kernel executes on its tile schedule: per (b, h) and query tile of 256
-    (q0 = 256 qt), each of the 8 waves runs 24 score MFMAs on tile 0, then 24 + 16 per key tile for
-    the nkt = (min(T, q0 + 256) - 1) // 64 + 1 key tiles up to the tile's last query (the last
-    iteration also scores one tile past the end, discarded), at 2 * 32 * 32 * 16 FLOP each."""
-    per_bh = 0
-    for qt in range((T + 255) // 256):
-        nkt = (min(T, 256 * qt + 256) - 1) // 64 + 1
-        per_bh += 8 * (24 + 40 * nkt)
-    return float(per_bh) * B * 128 * 2 * 32 * 32 * 16
+    with n scored key tiles (flagged_tiles), each of the 8 waves runs 24 score MFMAs on its first
+    tile, then 24 + 16 per tile (the last iteration also scores one tile more, discarded), at
+    2 * 32 * 32 * 16 FLOP each."""
+    per_b = 8 * (24 + 40 * np.asarray(tiles, np.int64))
+    return float(per_b.sum()) * 128 * 2 * 32 * 32 * 16
+
+
+def causal_tiles(T: int) -> int:
+    """Key tiles at or before the last query of each 256-query tile, summed over the tiles."""
+    return sum((min(T, 256 * qt + 256) - 1) // 64 + 1 for qt in range((T + 255) // 256))
+
+
+def window_attention_measurement(torch, mla, dev, stream, q, kv, k_pe, B: int, T: int, K: int,
+                                 scale: float) -> dict:
+    """The attention call on the benchmarked tensors with a selection that has locality: every
+    query selects its K most recent keys (itself included). Key tiles outside each query tile's
+    window hold no allowed key and are skipped, so the time follows the selected pairs rather
+    than the causal ones. Algorithmic FLOP = 640 x selected pairs x 128 heads."""
+    s = torch.arange(T, device=dev, dtype=torch.int32)[:, None]
+    win = s - torch.arange(K, device=dev, dtype=torch.int32)[None, :]
+    topk = torch.where(win < 0, torch.full_like(win, -1), win).expand(B, T, K).contiguous()
+    ws = torch.empty(mla.mla_attn_workspace_bytes(B, T, K), dtype=torch.uint8, device=dev)
+    mla.mla_attn_prepare(topk, ws)
+    out = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    us = timed_us(torch, stream, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale, out=out),
+                  reps=10, warm=3)
+    pairs = B * sum(min(K, t + 1) for t in range(T))
+    flop = 640.0 * pairs * 128
+    tiles = flagged_tiles(topk.cpu().numpy())
+    ex = executed_mfma_flop(tiles)
+    tf = flop / (us * 1e-6) / 1e12
+    del ws, out, topk
+    return {"selection": f"window of the {K} most recent keys", "us": us, "TFLOP_s": tf,
+            "frac_mfma": tf / PEAK_BF16_TFLOPS, "selected_pairs": pairs,
+            "scored_tiles": int(tiles.sum()), "causal_tiles": B * causal_tiles(T),
+            "executed_over_algorithmic": ex / flop}
 
 
 def sample_gfx_clock(torch, fn, reps: int) -> float | None:
@@ -461,6 +503,11 @@ def main():
         clock_mhz = sample_gfx_clock(torch, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale,
                                                                                          out=out), 400)
 
+    window = None
+    if kv is not None:
+        stream.wait_event(sync_ready)
+        window = window_attention_measurement(torch, mla, dev, stream, q, kv, k_pe, B, T, K, scale)
+
     if args.copy_calibration:
         src = torch.ones(1 << 26, dtype=torch.int32, device=dev)      # writes 256 MiB
         dst = torch.empty_like(src)
@@ -470,7 +517,8 @@ def main():
 
     pairs = selected_pairs(d["topk"])
     attn_flop = 640.0 * pairs * 128
-    exec_flop = executed_mfma_flop(B, T) if kv is not None else None
+    tiles = flagged_tiles(d["topk"]) if kv is not None else None
+    exec_flop = executed_mfma_flop(tiles) if kv is not None else None
     causal_pairs = B * T * (T + 1) // 2
     achieved = attn_flop / (att * 1e-3) / 1e12
     flop_down = 2.0 * B * T * 7168 * 576
@@ -511,6 +559,8 @@ def main():
                      "algorithmic_flop_per_launch": attn_flop,
                      "executed_mfma_flop_per_launch": exec_flop,
                      "executed_over_algorithmic": None if exec_flop is None else exec_flop / attn_flop,
+                     "scored_tiles": None if tiles is None else int(tiles.sum()),
+                     "causal_tiles": B * causal_tiles(T),
                      "measured_gfx_clock_mhz": clock_mhz,
                      "peak_at_measured_clock": None if clock_mhz is None else PEAK_BF16_TFLOPS * clock_mhz / 2400.0,
                      "frac_at_measured_clock": (None if clock_mhz is None else
@@ -521,6 +571,7 @@ def main():
         "attention_only_tokens_per_s": tokens / (att * 1e-3),
         "attention_mfma_busy_frac": mfma_busy_record() if headline else None,
         "bandwidth_kernels": side_meas,
+        "attention_window_selection": window,
         "selected_pairs_all_batches": pairs,
         "latent_mfma_flop_per_launch": (2176.0 * pairs * 128 + 2 * 2.0 * tokens * 128 * 128 * 512) if latent else None,
         "causal_over_selected": causal_pairs / pairs,

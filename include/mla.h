@@ -76,8 +76,9 @@ enum {
     MLA_E_SCRATCH = -9     /* beyond the fixed scratch of mla_sparse_prefill_attn_noalloc */
 };
 
-/* Bytes of device scratch mla_sparse_prefill_attn_noalloc holds on each device it runs on. */
-#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+/* Bytes of device scratch mla_sparse_prefill_attn_noalloc holds on each device it runs on: 32 MiB
+ * for the selection bitmap and 128 KiB for the key-tile flags. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((32u << 20) + (128u << 10))
 
 /*
  * Joint KV down-projection, latent RMSNorm and rotary key (one call for the front end).
@@ -296,7 +297,10 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
  * mla_sparse_prefill_attn in two calls, so that the selection step (which depends only on the
  * top-k indices) can run on another stream while the projections run:
  * mla_attn_prepare builds the selection bitmap (the excerpt's index mask intersected with the
- * causal mask, in the attention kernel's layout) into the workspace; it reads only topk.
+ * causal mask, in the attention kernel's layout) and, per 256 queries, a flag per 64-key tile
+ * that holds any allowed key, into the workspace; it reads only topk. The attention scores only
+ * flagged tiles: with a selection that leaves whole tiles empty (local or block-structured
+ * selections) the work shrinks with it.
  *   topk, B, T, K       as for mla_sparse_prefill_attn.
  *   workspace, ws_bytes (device, out) at least mla_attn_workspace_bytes(B, T, K) bytes.
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_WORKSPACE, MLA_E_ALIAS, MLA_E_DEVICE,
@@ -319,16 +323,18 @@ int mla_sparse_prefill_attn_prepared(const void* q, const void* kv, const void* 
 /*
  * mla_sparse_prefill_attn for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same kernels and result,
- * with the selection bitmap kept in a fixed device array of MLA_NOALLOC_SCRATCH_BYTES that the
- * library holds on each device for the life of the process, instead of a caller workspace. The
- * call allocates nothing (no hipMalloc, no library allocation) and only enqueues work.
+ * with the selection bitmap and key-tile flags kept in a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on each device for the life of the process,
+ * instead of a caller workspace. The call allocates nothing (no hipMalloc, no library allocation)
+ * and only enqueues work.
  *   q, kv, k_pe, topk, B, T, K, softmax_scale, out   as for mla_sparse_prefill_attn.
- * Limit: the bitmap, mla_noalloc_scratch_bytes(B, T) = 4 * B * (2 * ceil(T/64)) * (256 * ceil(T/256))
- * bytes, must fit the scratch (B * T^2 / 8 <= 32 MiB for T a multiple of 256: B <= 16 at T = 4096,
- * B = 1 at T = 16384); larger problems are rejected with MLA_E_SCRATCH before anything is enqueued.
+ * Limit: mla_noalloc_scratch_bytes(B, T) (the bitmap, 4 * B * (2 * ceil(T/64)) * (256 * ceil(T/256))
+ * bytes, then 4 * B * ceil(T/256) * ceil(T/2048) bytes of flags rounded up to 256) must fit the
+ * scratch (a bitmap of B * T^2 / 8 <= 32 MiB for T a multiple of 256: B <= 16 at T = 4096, B = 1 at
+ * T = 16384); larger problems are rejected with MLA_E_SCRATCH before anything is enqueued.
  * Every call on one device shares that device's scratch: calls that may overlap on one device
  * (different streams, or different threads without ordering) race, and must be serialised by the
- * caller. The scratch keeps the last call's bitmap; nothing in it has to start at zero.
+ * caller. The scratch keeps the last call's bitmap and flags; nothing in it has to start at zero.
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_ARG, MLA_E_ALIAS, MLA_E_SCRATCH, MLA_E_DEVICE,
  *         MLA_E_LAUNCH.
  */

@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla.so")
+# MLA_LIBRARY names another build of the same library (the host-sanitizer build of the checks
+# uses it); by default the in-tree libmla.so.
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_PKG, "libmla.so")
 
 HIDDEN, KV_LORA, ROPE, KV_A_OUT = 7168, 512, 64, 576
 HEADS, QK_NOPE, QK_HEAD, V_HEAD = 128, 128, 192, 128
@@ -436,7 +438,7 @@ def mla_sparse_prefill_attn(q, kv, k_pe, topk, softmax_scale: float | None = Non
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = (32 << 20) + (128 << 10)
 
 
 def mla_noalloc_scratch_bytes(B: int, T: int) -> int:

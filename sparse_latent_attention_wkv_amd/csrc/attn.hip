@@ -6,15 +6,17 @@
 // except at the indexer's top-k positions, plus the causal mask, is added to every head's
 // scores; softmax over keys; the weights mix the values.
 //
-// Two kernels:
+// Three kernels:
 //  * sel_bitmap: the index mask plus causal mask as bits, bitmap[b][t/32][s] bit t%32, shared by
 //    all heads (one bit per (query, key) instead of a T x T float tensor).
+//  * tile_flags: per 256-query tile, one bit per 64-key tile that holds an allowed key for at
+//    least one of its queries.
 //  * sparse_attn: flash-style attention on a persistent grid (one workgroup per compute unit)
-//    that walks work items (b, h, a tile of 256 queries) in a fixed order; key tiles of 64 are
-//    staged in LDS (key and value rows as stored); every key tile at or before a wave's queries
-//    is scored and keys outside the selection are masked to -inf, so they get exactly zero
-//    weight. Online softmax in fp32 (running max and sum per query, base-2 exponentials), bf16
-//    MFMA for q.k and p.v with fp32 accumulation.
+//    that walks work items (b, h, a tile of 256 queries) in a fixed order; of the key tiles at or
+//    before the item's queries, those whose flag is set are staged in LDS (key and value rows as
+//    stored) and scored, and keys outside the selection are masked to -inf, so they get exactly
+//    zero weight; tiles without a flag are skipped. Online softmax in fp32 (running max and sum
+//    per query, base-2 exponentials), bf16 MFMA for q.k and p.v with fp32 accumulation.
 //
 // MFMA formulation: S^T = K . Q^T (32 keys x 32 queries per block), so lane l owns query
 // (l % 32) and 16 of the block's keys; the row max and row sum are in-lane plus one exchange
@@ -87,6 +89,30 @@ hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout,
 }
 
 // ------------------------------------------------------------------------------------------------
+// Tile flags: bit (kt % 32) of flags[b][qt][kt / 32] is set when some query of the 256-query tile
+// qt has an allowed key among the 64 keys of tile kt, i.e. when one of the words 2kt, 2kt+1 of one
+// of its bitmap columns is nonzero. Block (qt, g, b) covers key tiles 32g..32g+31; thread j reads
+// column qt*256 + j of their 64 words (each wave load is 256 consecutive bytes).
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_flags_kernel(const uint32_t* __restrict__ bitmap, int Wp, int Tpad,
+                                                         int nqt, int FW, uint32_t* __restrict__ flags) {
+    __shared__ uint32_t part[4];
+    const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int w0 = 64 * g;
+    const int nw = min(64, Wp - w0);
+    const uint32_t* col = bitmap + ((size_t)b * Wp + w0) * Tpad + (size_t)qt * 256 + threadIdx.x;
+    uint32_t bits = 0;
+#pragma unroll 8
+    for (int i = 0; i < nw; ++i)
+        if (col[(size_t)i * Tpad] != 0u) bits |= 1u << (i >> 1);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) bits |= (uint32_t)__shfl_xor((int)bits, off, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = bits;
+    __syncthreads();
+    if (threadIdx.x == 0) flags[((size_t)b * nqt + qt) * FW + g] = part[0] | part[1] | part[2] | part[3];
+}
+
+// ------------------------------------------------------------------------------------------------
 // Attention.
 // ------------------------------------------------------------------------------------------------
 // Work item: 8 waves (two per SIMD) x 32 queries = 256 queries of one (b, h); a workgroup runs
@@ -118,6 +144,7 @@ constexpr int kKT = 64;
 constexpr int kWaves = 8;
 constexpr int kQW = 32;                  // queries per wave
 constexpr int kQT = kWaves * kQW;        // 256 queries per workgroup
+constexpr int kMaxKeyTiles = 32768 / kKT; // key tiles of the longest accepted sequence
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -202,9 +229,11 @@ __device__ __forceinline__ void sm_exp(const f32x16 s[2], float mx, float c2, fl
 __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const uint16_t* __restrict__ kpe,
-                                                          const uint32_t* __restrict__ bitmap, int T,
-                                                          int Tpad, int Wp, int nqt, int BH, int npairs,
-                                                          int units, float c2, uint16_t* __restrict__ out) {
+                                                          const uint32_t* __restrict__ bitmap,
+                                                          const uint32_t* __restrict__ tflags, int T,
+                                                          int Tpad, int Wp, int FW, int nqt, int BH,
+                                                          int npairs, int units, float c2,
+                                                          uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t knA[kKT * 128], knB[kKT * 128], knC[kKT * 128];
     __shared__ __attribute__((aligned(16))) uint16_t kpA[kKT * 64], kpB[kKT * 64], kpC[kKT * 64];
     __shared__ __attribute__((aligned(16))) uint16_t vA[kKT * 128], vB[kKT * 128], vC[kKT * 128];
@@ -212,6 +241,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     // each thread's fixed load offsets (four key/value rows, one rotary row), kept in LDS rather
     // than in registers: they are read once per tile
     __shared__ __attribute__((aligned(16))) uint32_t off_lds[kWaves * 64 * 5];
+    // the item's key tiles to score, ascending, and their count; the flag rows of the current
+    // and the next item (lane l of wave 0 loads word min(l, FW - 1) of a row)
+    __shared__ uint16_t kt_list[kMaxKeyTiles];
+    __shared__ int kt_count;
+    __shared__ uint32_t flag_lds[2][64];
     const Stage stA{knA, kpA, vA, bmA, lds_addr(knA), lds_addr(kpA), lds_addr(vA), lds_addr(bmA)};
     const Stage stB{knB, kpB, vB, bmB, lds_addr(knB), lds_addr(kpB), lds_addr(vB), lds_addr(bmB)};
     const Stage stC{knC, kpC, vC, bmC, lds_addr(knC), lds_addr(kpC), lds_addr(vC), lds_addr(bmC)};
@@ -221,16 +255,40 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     const int half = lane >> 5, col = lane & 31;
 
     // Persistent schedule. A unit is a pair of query tiles of one (b, h): tile nqt-1-p (the
-    // longer) then tile p, so every unit costs about the same number of key tiles. Workgroups
-    // are dealt to the 8 XCDs round-robin, so workgroup w sits on XCD w % 8 and takes the
-    // units u = w, w + G, ... (G a multiple of 8), all of that XCD: unit u covers head
-    // bh = u % 8 + 8 * (k / npairs), pair k % npairs, k = u / 8. The workgroups of one XCD run
-    // the pairs of a few heads side by side and in step, so those heads' keys and values are
-    // shared through that XCD's L2.
+    // longer) then tile p, so under the causal mask every unit costs about the same number of
+    // key tiles. Workgroups are dealt to the 8 XCDs round-robin, so workgroup w sits on XCD
+    // w % 8 and takes the units u = w, w + G, ... (G a multiple of 8), all of that XCD: unit u
+    // covers head bh = u % 8 + 8 * g and the pair (k % npairs + j0) % npairs, k = u / 8,
+    // g = k / npairs, where j0 is the step (u0 / G) at which the head's first unit u0 runs. The
+    // workgroups of one XCD run the pairs of a few heads side by side and in step, so those heads'
+    // keys and values are shared through that XCD's L2; the rotation by j0 hands a workgroup a
+    // different pair at each step (every pair once when npairs divides G / 8), so when skipped
+    // key tiles make the pairs' costs differ, the workgroups' totals still even out.
+    // (BH is a multiple of 8, so every unit names a head below BH.)
+    auto unit_of = [&](int u, int& bh, int& pr) {
+        const int k_ = u >> 3;
+        const int grp = k_ / npairs;
+        bh = (u & 7) + 8 * grp;
+        const int j0 = ((u & 7) + 8 * grp * npairs) / (int)gridDim.x;
+        pr = (k_ - grp * npairs + j0) % npairs;
+    };
+    // Wave 0 loads each item's row of key-tile flags into LDS one item ahead (the first one here),
+    // so building an item's tile list waits for no global load: a row loaded during an item has
+    // landed by that item's first tile-end wait.
+    auto load_flags = [&](int slot, int fb, int fqt) {
+        dma4_lds(tflags + ((size_t)fb * nqt + fqt) * FW, (uint32_t)min(lane, FW - 1) * 4u,
+                 lds_addr(&flag_lds[slot][0]));
+    };
+    if (wave == 0) {
+        int bh0, pr0;
+        unit_of(blockIdx.x, bh0, pr0);
+        load_flags(0, bh0 / kHeads, nqt - 1 - pr0);
+        wait_vm0();
+    }
+    int fslot = 0;
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int k_ = u >> 3;
-    const int bh = (u & 7) + 8 * (k_ / npairs);
-    const int pr = k_ - (k_ / npairs) * npairs;
+    int bh, pr;
+    unit_of(u, bh, pr);
     if (bh >= BH) continue;
     const int b = bh / kHeads, h = bh - b * kHeads;
     for (int item = 0; item < 2; ++item) {
@@ -262,40 +320,40 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     // consecutive LDS; the swizzle is applied by choosing which source chunk each lane fetches.
     //   waves 0-3: kn rows 16w..16w+15 (4 instructions); waves 4-7: v rows 16(w-4).. (4);
     //   every wave: kp rows 8w..8w+7 (1); waves 0-1: bm word w of the tile (1).
-    // Per-lane source offsets (elements from the tile's first row) are fixed; only the last
-    // tile, whose rows may run past the sequence, clamps rows to the last key (never selected).
+    // Per-lane byte offsets are taken from the head's (or sequence's) first row, so the scalar
+    // bases stay fixed and only the tile's first key t0 enters each offset; a row past the
+    // sequence (last tile only) is clamped to the last key (never selected). Offsets stay below
+    // 2^32: at most 32768 rows of 512 bytes, and 2 * ceil(T/64) * Tpad * 4 bytes of bitmap.
     const int r16 = lane >> 4;
-    uint32_t src_off[4];   // bytes from the tile's first row
+    uint32_t chunk_off[4];   // bytes within the key row
     const bool kn_wave = wave < 4;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int row = 16 * (wave & 3) + 4 * k + r16;
         const int lc = kn_wave ? (lane & 15) ^ ((4 * k + r16) & 15) : (lane & 15) ^ (4 * r16);
-        src_off[k] = (uint32_t)(row * 512 + lc * 16 + (kn_wave ? 0 : 2 * kNope));
+        chunk_off[k] = (uint32_t)(lc * 16 + (kn_wave ? 0 : 2 * kNope));
     }
     const int kp_row = 8 * wave + (lane >> 3);
     {
-        const uint32_t kp_off0 = (uint32_t)(kp_row * 2 * kRope + (((lane & 7) ^ ((kp_row >> 1) & 7)) << 4));
-        *reinterpret_cast<u32x4*>(off_lds + 4 * tid) = u32x4{src_off[0], src_off[1], src_off[2], src_off[3]};
-        off_lds[kWaves * 64 * 4 + tid] = kp_off0;
+        const uint32_t kp_chunk = (uint32_t)(((lane & 7) ^ ((kp_row >> 1) & 7)) << 4);
+        *reinterpret_cast<u32x4*>(off_lds + 4 * tid) = u32x4{chunk_off[0], chunk_off[1], chunk_off[2], chunk_off[3]};
+        off_lds[kWaves * 64 * 4 + tid] = kp_chunk;
     }
     auto issue_tile = [&](const Stage& st, int kt) {
-        const u32x4 src_o = *reinterpret_cast<const u32x4*>(off_lds + 4 * tid);
-        const uint32_t kp_off = off_lds[kWaves * 64 * 4 + tid];
+        const u32x4 ch = *reinterpret_cast<const u32x4*>(off_lds + 4 * tid);
+        const uint32_t kp_ch = off_lds[kWaves * 64 * 4 + tid];
         const int t0 = kt * kKT;
         const uint32_t dst = kn_wave ? st.kn_l : st.v_l;
-        const int tl = T - 1 - t0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int row = 16 * (wave & 3) + 4 * k + r16;
-            const int dr = min(row, tl) - row;
-            dma16_lds(kvh + (size_t)t0 * 256, src_o[k] + (uint32_t)(dr * 512),
+            dma16_lds(kvh, (uint32_t)min(t0 + row, T - 1) * 512u + ch[k],
                       dst + (uint32_t)((16 * (wave & 3) + 4 * k) * 128 * 2));
         }
-        const int drp = min(kp_row, tl) - kp_row;
-        dma16_lds(kpeb + (size_t)t0 * kRope, kp_off + (uint32_t)(drp * 2 * kRope), st.kp_l + (uint32_t)(8 * wave * 64 * 2));
+        dma16_lds(kpeb, (uint32_t)min(t0 + kp_row, T - 1) * (2u * kRope) + kp_ch,
+                  st.kp_l + (uint32_t)(8 * wave * 64 * 2));
         if (wave < 2)
-            dma16_lds(bmb + (size_t)(kt * 2 + wave) * Tpad + q0, (uint32_t)lane * 16, st.bm_l + (uint32_t)(wave * kQT * 4));
+            dma16_lds(bmb + q0, (uint32_t)((kt * 2 + wave) * Tpad) * 4u + (uint32_t)lane * 16,
+                      st.bm_l + (uint32_t)(wave * kQT * 4));
     };
 
     // ---- per-lane LDS read offsets (bytes).
@@ -369,8 +427,13 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     // One tile t in stage `cur` (values) with tile t+1 in `nxt` (keys, selection bits) and tile
     // t+2 loading into `ld`.
     //   X_t: S(t+1) MFMAs | exponentials of t;  rare O rescale;  Y_t: P.V of t | mask, max of t+1
-    auto tile = [&](int kt, int nkt, const Stage& cur, const Stage& nxt, const Stage& ld) {
-        if (kt + 2 < nkt) issue_tile(ld, kt + 2);
+    // Key tile to load at the start of tile i (entry i + 2 of the list), read from LDS at the start
+    // of the tile before, so the read completes under that tile's work.
+    int kt_ahead = 0;
+    auto tile = [&](int i, int n, const Stage& cur, const Stage& nxt, const Stage& ld) {
+        const int kt_load = __builtin_amdgcn_readfirstlane(kt_ahead);
+        kt_ahead = kt_list[min(i + 3, n - 1)];
+        if (i + 2 < n) issue_tile(ld, kt_load);
         f32x16 s_nx[2];
         bf16x8 pf[2][2];
         float alpha;
@@ -390,21 +453,61 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
         __syncthreads();
     };
 
+    // Key tiles at or before the item's last query whose flag is set, listed in ascending order by
+    // wave 0 (lane l looks at tiles 8l..8l+7). An item without any allowed key gets the list {0}:
+    // tile 0's selection bits are then all clear, so every weight is zero and its rows are zeros.
     const int q_last = min(T, q0 + kQT) - 1;
     const int nkt = q_last / kKT + 1;
+    if (wave == 0) {
+        const int t8 = 8 * lane;
+        uint32_t f = 0;
+        if (t8 < nkt) {
+            f = (flag_lds[fslot][lane >> 2] >> (8 * (lane & 3))) & 0xFFu;
+            if (nkt - t8 < 8) f &= (1u << (nkt - t8)) - 1u;
+        }
+        // the next item: tile pr of this unit, else the first tile of the workgroup's next unit
+        if (item == 0 && pr != nqt - 1 - pr) {
+            load_flags(fslot ^ 1, b, pr);
+        } else if (u + (int)gridDim.x < units) {
+            int nbh, npr;
+            unit_of(u + (int)gridDim.x, nbh, npr);
+            load_flags(fslot ^ 1, nbh / kHeads, nqt - 1 - npr);
+        }
+        const int c = __builtin_popcount(f);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        int pos = incl - c;
+        while (f) {
+            kt_list[pos++] = (uint16_t)(t8 + __builtin_ctz(f));
+            f &= f - 1u;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (lane == 0) {
+            if (total == 0) kt_list[0] = 0;
+            kt_count = total > 0 ? total : 1;
+        }
+    }
+    fslot ^= 1;
+    __syncthreads();
+    const int n = __builtin_amdgcn_readfirstlane(kt_count);
 
-    issue_tile(stA, 0);
-    if (nkt > 1) issue_tile(stB, 1);
+    issue_tile(stA, __builtin_amdgcn_readfirstlane((int)kt_list[0]));
+    if (n > 1) issue_tile(stB, __builtin_amdgcn_readfirstlane((int)kt_list[1]));
+    kt_ahead = kt_list[min(2, n - 1)];
     wait_vm0();
     __syncthreads();
     s_tile(stA, s_cur);
     mx_cur = mask_tile(stA, s_cur);
-    for (int kt = 0; kt < nkt; kt += 3) {
-        tile(kt, nkt, stA, stB, stC);
-        if (kt + 1 >= nkt) break;
-        tile(kt + 1, nkt, stB, stC, stA);
-        if (kt + 2 >= nkt) break;
-        tile(kt + 2, nkt, stC, stA, stB);
+    for (int i = 0; i < n; i += 3) {
+        tile(i, n, stA, stB, stC);
+        if (i + 1 >= n) break;
+        tile(i + 1, n, stB, stC, stA);
+        if (i + 2 >= n) break;
+        tile(i + 2, n, stC, stA, stB);
     }
 
     // Epilogue: the two lane halves hold partial sums over different keys of the same query.
@@ -429,9 +532,25 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 
 int attn_bitmap_words(int T) { return 2 * ((T + kKT - 1) / kKT); }
 int attn_bitmap_cols(int T) { return (T + kQT - 1) / kQT * kQT; }
+int attn_flag_words(int T) { return ((T + kKT - 1) / kKT + 31) / 32; }
+size_t attn_select_bytes(int B, int T) {
+    const size_t bm = (size_t)B * attn_bitmap_words(T) * attn_bitmap_cols(T) * 4;
+    const size_t fl = (size_t)B * ((T + kQT - 1) / kQT) * attn_flag_words(T) * 4;
+    return bm + ((fl + 255) & ~(size_t)255);
+}
+
+hipError_t launch_attn_select(const int32_t* topk, int B, int T, int K, uint32_t* sel, hipStream_t stream) {
+    const int Wp = attn_bitmap_words(T), Tpad = attn_bitmap_cols(T);
+    hipError_t e = launch_sel_bitmap(topk, B, T, K, Wp, Tpad, sel, stream);
+    if (e != hipSuccess) return e;
+    const int nqt = Tpad / kQT, FW = attn_flag_words(T);
+    tile_flags_kernel<<<dim3(nqt, FW, B), 256, 0, stream>>>(sel, Wp, Tpad, nqt, FW,
+                                                           sel + (size_t)B * Wp * Tpad);
+    return hipGetLastError();
+}
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint16_t* k_pe,
-                              const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
+                              const uint32_t* sel, int B, int T, float scale, uint16_t* out,
                               hipStream_t stream) {
     const int nqt = (T + kQT - 1) / kQT;
     const int npairs = (nqt + 1) / 2;
@@ -445,8 +564,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint1
     }
     const int G = min(units, cus / 8 * 8);
     const float c2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-    sparse_attn_kernel<<<G, kWaves * 64, 0, stream>>>(q, kv, k_pe, bitmap, T, attn_bitmap_cols(T),
-                                                      attn_bitmap_words(T), nqt, BH, npairs, units, c2, out);
+    const int Wp = attn_bitmap_words(T), Tpad = attn_bitmap_cols(T);
+    sparse_attn_kernel<<<G, kWaves * 64, 0, stream>>>(q, kv, k_pe, sel, sel + (size_t)B * Wp * Tpad, T, Tpad,
+                                                      Wp, attn_flag_words(T), nqt, BH, npairs, units, c2,
+                                                      out);
     return hipGetLastError();
 }
 

@@ -774,7 +774,7 @@ AutoWorkspace auto_workspace(int B, int T, int K) {
     const size_t nseq = a.split == T ? (size_t)B : 1;
     size_t off = 0;
     a.kv = off;       off += align256(nseq * kHeads * a.split * 256 * 2);
-    a.bitmap = off;   off += align256(nseq * attn_bitmap_words(a.split) * attn_bitmap_cols(a.split) * 4);
+    a.bitmap = off;   off += align256(attn_select_bytes((int)nseq, a.split));
     a.latent = off;   off += a.split < T ? latent_workspace(B, T, K, a.split).bytes : 0;
     a.bytes = off;
     return a;
@@ -790,9 +790,7 @@ hipError_t launch_sparse_attn_auto(const uint16_t* q, const uint16_t* c_kv, cons
     hipError_t e = hipSuccess;
     if (a.split == T) {   // the head-major path for every row, all sequences at once
         if ((e = launch_gemm_kv_up(c_kv, w_ukv, B, T, kvp, stream)) != hipSuccess) return e;
-        if ((e = launch_sel_bitmap(topk, B, T, K, attn_bitmap_words(T), attn_bitmap_cols(T), bm, stream)) !=
-            hipSuccess)
-            return e;
+        if ((e = launch_attn_select(topk, B, T, K, bm, stream)) != hipSuccess) return e;
         return launch_sparse_attn(q, kvp, k_pe, bm, B, T, scale, out, stream);
     }
     // rows 0..split-1 of sequence b are a contiguous prefix of each per-token tensor, so each
@@ -800,9 +798,7 @@ hipError_t launch_sparse_attn_auto(const uint16_t* q, const uint16_t* c_kv, cons
     for (int b = 0; b < B && a.split > 0; ++b) {
         const int S = a.split;
         if ((e = launch_gemm_kv_up(c_kv + (size_t)b * T * kLora, w_ukv, 1, S, kvp, stream)) != hipSuccess) return e;
-        if ((e = launch_sel_bitmap(topk + (size_t)b * T * K, 1, S, K, attn_bitmap_words(S), attn_bitmap_cols(S), bm,
-                                   stream)) != hipSuccess)
-            return e;
+        if ((e = launch_attn_select(topk + (size_t)b * T * K, 1, S, K, bm, stream)) != hipSuccess) return e;
         if ((e = launch_sparse_attn(q + (size_t)b * T * kHeads * kQkHead, kvp, k_pe + (size_t)b * T * kRope, bm, 1, S,
                                     scale, out + (size_t)b * T * kHeads * kVHead, stream)) != hipSuccess)
             return e;

@@ -143,14 +143,13 @@ int validate_topk(const int32_t* topk, int B, int T, int K) {
     return MLA_OK;
 }
 
-// Bitmap as the attention kernel reads it (padded so every staged tile is in bounds).
-size_t attn_bitmap_bytes(int B, int T) {
-    return (size_t)B * mla::attn_bitmap_words(T) * mla::attn_bitmap_cols(T) * sizeof(uint32_t);
-}
+// Selection data as the attention kernel reads it: the bitmap (padded so every staged tile is in
+// bounds) and the key-tile flags.
+size_t attn_bitmap_bytes(int B, int T) { return mla::attn_select_bytes(B, T); }
 // Bitmap as mla_selection_bitmap returns it, [B][ceil(T/32)][T].
 size_t plain_bitmap_bytes(int B, int T) { return (size_t)B * ((T + 31) / 32) * T * sizeof(uint32_t); }
 
-// Scratch of mla_sparse_prefill_attn_noalloc: the selection bitmap lives in this fixed array
+// Scratch of mla_sparse_prefill_attn_noalloc: the selection bitmap and key-tile flags live in this fixed array
 // instead of a caller workspace. Each device holds its own copy for the life of the process. In
 // host code `scratch` names a host-side stand-in, not the device copy: the device address comes
 // from hipGetSymbolAddress, once per device, and only that address is handed to kernels.
@@ -383,9 +382,8 @@ int mla_attn_prepare(const int32_t* topk, int B, int T, int K, void* workspace, 
     const Span outs[] = {{workspace, attn_bitmap_bytes(B, T)}};
     if (any_alias(outs, 1, ins, 1)) return MLA_E_ALIAS;
     if ((st = check_device()) != MLA_OK) return st;
-    return launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
-                                           mla::attn_bitmap_cols(T), static_cast<uint32_t*>(workspace),
-                                           static_cast<hipStream_t>(stream)));
+    return launched(mla::launch_attn_select(topk, B, T, K, static_cast<uint32_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -440,8 +438,7 @@ int mla_sparse_prefill_attn(const void* q, const void* kv, const void* k_pe, con
     if ((st = check_device()) != MLA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t* bm = static_cast<uint32_t*>(workspace);
-    st = launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
-                                         mla::attn_bitmap_cols(T), bm, s));
+    st = launched(mla::launch_attn_select(topk, B, T, K, bm, s));
     if (st != MLA_OK) return st;
     return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
                                             static_cast<const uint16_t*>(kv),
@@ -481,11 +478,10 @@ int mla_sparse_prefill_attn_noalloc(const void* q, const void* kv, const void* k
     if (hipGetDevice(&dev) != hipSuccess) return MLA_E_DEVICE;
     uint32_t* bm = static_cast<uint32_t*>(scratch_address(dev));
     if (!bm) return MLA_E_DEVICE;
-    // every word of the bitmap region the attention reads is written by the bitmap kernel
-    // (zeros past the sequence), so the scratch needs no clearing between calls
+    // every word of the bitmap and flag regions the attention reads is written by the selection
+    // kernels (bitmap zeros past the sequence), so the scratch needs no clearing between calls
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = launched(mla::launch_sel_bitmap(topk, B, T, K, mla::attn_bitmap_words(T),
-                                         mla::attn_bitmap_cols(T), bm, s));
+    st = launched(mla::launch_attn_select(topk, B, T, K, bm, s));
     if (st != MLA_OK) return st;
     return launched(mla::launch_sparse_attn(static_cast<const uint16_t*>(q),
                                             static_cast<const uint16_t*>(kv),

@@ -85,6 +85,14 @@ __device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint
                  : "v"(voff), "s"(uniform_ptr(sbase)), "s"(uniform32(lds))
                  : "memory", "m0");
 }
+// 4-byte form: lane l's 4 bytes at sbase + voff land at LDS address lds + 4 l
+// (global_load_lds_dword).
+__device__ __forceinline__ void dma4_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(uniform32(lds))
+                 : "memory", "m0");
+}
 // 32-bit LDS byte address of an LDS object.
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {

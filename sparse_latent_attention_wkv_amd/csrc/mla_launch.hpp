@@ -42,8 +42,14 @@ hipError_t launch_check_topk(const int32_t* topk, int B, int T, int K, int64_t* 
 // Bitmap geometry the attention kernel reads: words per query column and query columns.
 int attn_bitmap_words(int T);
 int attn_bitmap_cols(int T);
+// Words of key-tile flags per 256-query tile.
+int attn_flag_words(int T);
+// The attention's selection data: the bitmap [B][attn_bitmap_words][attn_bitmap_cols] followed by
+// the key-tile flags [B][ceil(T/256)][attn_flag_words]; bytes, and the two kernels that write it.
+size_t attn_select_bytes(int B, int T);
+hipError_t launch_attn_select(const int32_t* topk, int B, int T, int K, uint32_t* sel, hipStream_t stream);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* kv, const uint16_t* k_pe,
-                              const uint32_t* bitmap, int B, int T, float scale, uint16_t* out,
+                              const uint32_t* sel, int B, int T, float scale, uint16_t* out,
                               hipStream_t stream);
 
 

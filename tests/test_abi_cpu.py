@@ -47,10 +47,12 @@ def test_host_only_helpers():
     for code in range(-9, 0):
         assert lib.mla_status_string(code).startswith(b"MLA_E_")
     assert b"gfx950" in lib.mla_build_info()
-    # bitmap words: B * (2 * ceil(T/64)) words x (256 * ceil(T/256)) query columns x 4 bytes
-    assert lib.mla_attn_workspace_bytes(2, 4096, 2048) == 2 * 128 * 4096 * 4
-    assert lib.mla_attn_workspace_bytes(1, 100, 7) == 4 * 256 * 4
-    assert lib.mla_attn_workspace_bytes(3, 16384, 2048) == 3 * 512 * 16384 * 4
+    # bitmap: B * (2 * ceil(T/64)) words x (256 * ceil(T/256)) query columns x 4 bytes; then the
+    # key-tile flags, B * ceil(T/256) * ceil(ceil(T/64) / 32) words, rounded up to 256 bytes
+    assert lib.mla_attn_workspace_bytes(2, 4096, 2048) == 2 * 128 * 4096 * 4 + 256
+    assert lib.mla_attn_workspace_bytes(1, 100, 7) == 4 * 256 * 4 + 256
+    assert lib.mla_attn_workspace_bytes(3, 16384, 2048) == 3 * 512 * 16384 * 4 + 3 * 64 * 8 * 4
+    assert lib.mla_attn_workspace_bytes(1, 32768, 2048) == 1024 * 32768 * 4 + 128 * 16 * 4
     assert lib.mla_attn_workspace_bytes(0, 4096, 2048) == 0
     assert lib.mla_attn_workspace_bytes(1, 40000, 2048) == 0
     assert lib.mla_last_hip_error() == 0
@@ -150,9 +152,11 @@ def test_check_topk_validation():
 
 def test_noalloc_attention_validation():
     lib = _lib()
-    assert mla.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert mla.NOALLOC_SCRATCH_BYTES == (32 << 20) + (128 << 10)
     assert lib.mla_noalloc_scratch_bytes(2, 4096) == lib.mla_attn_workspace_bytes(2, 4096, 2048)
-    assert lib.mla_noalloc_scratch_bytes(1, 16384) == 32 << 20
+    assert lib.mla_noalloc_scratch_bytes(1, 16384) == (32 << 20) + 2048
+    assert lib.mla_noalloc_scratch_bytes(16, 4096) <= mla.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_noalloc_scratch_bytes(17, 4096) > mla.NOALLOC_SCRATCH_BYTES
     assert lib.mla_noalloc_scratch_bytes(0, 64) == 0
 
     def call(q=A, kv=B_, kpe=C, topk=D, B=1, T=64, K=16, scale=0.135, out=E):
@@ -215,9 +219,10 @@ def test_auto_split_and_validation():
     assert lib.mla_attn_auto_split(300, 40) == 0                # every row in the latent form
     assert lib.mla_attn_auto_split(0, 16) == -1
     assert lib.mla_attn_auto_workspace_bytes(0, 64, 16) == 0
-    # all head-major: per-head keys/values and bitmap of both sequences, no latent part
+    # all head-major: per-head keys/values, bitmap and key-tile flags of both sequences, no
+    # latent part
     ws = lib.mla_attn_auto_workspace_bytes(2, 4096, 2048)
-    assert ws == 2 * (128 * 4096 * 256 * 2 + 128 * 4096 * 4)
+    assert ws == 2 * (128 * 4096 * 256 * 2 + 128 * 4096 * 4) + 256
     GB = 1 << 30
     Q, CKV, KPE, W, TK, OUT, WS = (GB * i for i in range(1, 8))
     wsb = lib.mla_attn_auto_workspace_bytes(1, 1100, 100)
