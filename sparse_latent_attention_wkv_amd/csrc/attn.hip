@@ -91,15 +91,16 @@ hipError_t launch_sel_bitmap(const int32_t* topk, int B, int T, int K, int Wout,
 // ------------------------------------------------------------------------------------------------
 // Tile flags: bit (kt % 32) of flags[b][qt][kt / 32] is set when some query of the 256-query tile
 // qt has an allowed key among the 64 keys of tile kt, i.e. when one of the words 2kt, 2kt+1 of one
-// of its bitmap columns is nonzero. Block (qt, g, b) covers key tiles 32g..32g+31; thread j reads
-// column qt*256 + j of their 64 words (each wave load is 256 consecutive bytes).
+// of its bitmap columns is nonzero. Block (qt, g, b) writes byte g of the row (key tiles
+// 8g..8g+7; zero for tiles past the sequence); thread j reads column qt*256 + j of their 16
+// words (each wave load is 256 consecutive bytes).
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tile_flags_kernel(const uint32_t* __restrict__ bitmap, int Wp, int Tpad,
-                                                         int nqt, int FW, uint32_t* __restrict__ flags) {
+                                                         int nqt, int FW, uint8_t* __restrict__ flags) {
     __shared__ uint32_t part[4];
     const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int w0 = 64 * g;
-    const int nw = min(64, Wp - w0);
+    const int w0 = 16 * g;
+    const int nw = max(0, min(16, Wp - w0));
     const uint32_t* col = bitmap + ((size_t)b * Wp + w0) * Tpad + (size_t)qt * 256 + threadIdx.x;
     uint32_t bits = 0;
 #pragma unroll 8
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(256) void tile_flags_kernel(const uint32_t* __restr
     for (int off = 32; off >= 1; off >>= 1) bits |= (uint32_t)__shfl_xor((int)bits, off, 64);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = bits;
     __syncthreads();
-    if (threadIdx.x == 0) flags[((size_t)b * nqt + qt) * FW + g] = part[0] | part[1] | part[2] | part[3];
+    if (threadIdx.x == 0)
+        flags[((size_t)b * nqt + qt) * FW * 4 + g] = (uint8_t)(part[0] | part[1] | part[2] | part[3]);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -544,8 +546,8 @@ hipError_t launch_attn_select(const int32_t* topk, int B, int T, int K, uint32_t
     hipError_t e = launch_sel_bitmap(topk, B, T, K, Wp, Tpad, sel, stream);
     if (e != hipSuccess) return e;
     const int nqt = Tpad / kQT, FW = attn_flag_words(T);
-    tile_flags_kernel<<<dim3(nqt, FW, B), 256, 0, stream>>>(sel, Wp, Tpad, nqt, FW,
-                                                           sel + (size_t)B * Wp * Tpad);
+    tile_flags_kernel<<<dim3(nqt, 4 * FW, B), 256, 0, stream>>>(
+        sel, Wp, Tpad, nqt, FW, reinterpret_cast<uint8_t*>(sel + (size_t)B * Wp * Tpad));
     return hipGetLastError();
 }
 
