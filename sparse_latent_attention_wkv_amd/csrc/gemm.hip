@@ -237,153 +237,100 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
 }
 
 // ------------------------------------------------------------------------------------------------
-// Up-projection GEMM, second form: BM tokens x 256 features (one head) per workgroup of BM/32
-// waves (BM/64 along tokens x 2 along features), each wave 64 x 128. K streams in chunks of 32
-// through a three-stage LDS ring filled by direct global->LDS loads issued two chunks ahead: no
-// staging registers. LDS rows are 64 bytes (32 bf16); 16-byte chunk c of row r is stored at
-// c ^ ((r >> 2) & 3), which keeps the 16-lane operand reads conflict free. The epilogue stages
-// each wave's bf16 blocks in LDS so every global store writes whole 256-byte half rows.
-// BM = 128 (four waves, 72 KB: two workgroups share a CU) or 256 (eight waves, 96 KB: operands
-// reused over twice the tokens).
+// Up-projection GEMM: one head's 256 features x 256 tokens per workgroup of eight waves (4 along
+// tokens x 2 along features), each wave 64 x 128: eight 32x32 accumulators. K = 512 streams in
+// 8 chunks of 64 through a two-stage LDS ring (256 X rows and 256 W rows of 128 bytes, 64 KB per
+// stage) filled by direct global->LDS loads one chunk ahead; every row
+// piece a load fetches is one whole 128-byte line (32-deep chunks fetched half lines, each line
+// twice, and ran 4% slower). 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16 lanes
+// of an operand read hit 16 distinct bank groups. The epilogue stages each wave's 32 x 128 bf16
+// blocks in its own 8 KB of the idle ring and writes whole 256-byte half rows of kv[b][h][t].
 // ------------------------------------------------------------------------------------------------
-#ifndef UP_BM
-#define UP_BM 256
-#endif
-namespace up2 {
-#ifndef UP_STAGES
-#define UP_STAGES 3
-#endif
-constexpr int BN = 256, BK = 32, STAGES = UP_STAGES;
-constexpr int ROWB = BK * 2;                                 // 64 bytes per LDS row
-constexpr int WB = BN * ROWB;                                // 16 KB of W rows per stage
+namespace up {
+constexpr int BM = 256, BN = 256, BK = 64, ROWB = BK * 2;
+constexpr int XB = BM * ROWB, SB = XB + BN * ROWB;   // 64 KB per stage
+constexpr int NK = kLora / BK, LOADS = 8;            // chunks; 1 KB loads per wave per chunk
+__device__ __forceinline__ int key(int r) { return (r >> 1) & 7; }
 }
 
-__device__ __forceinline__ void dma16_g(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
-
-template <int BM>
-__global__ __launch_bounds__(BM * 2) void gemm_up_kernel(const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ W, int M, int T,
-                                                         int mtiles, uint16_t* __restrict__ out) {
-    using namespace up2;
-    constexpr int NW = BM / 32;                  // waves
-    constexpr int XB = BM * ROWB;                // X rows per stage
-    constexpr int WLOADS = 16 / NW;              // 1 KB W loads per wave per chunk
-    constexpr int LOADS = 2 + WLOADS;            // loads per wave per chunk (2 of X)
-    __shared__ __attribute__((aligned(16))) uint8_t xs0[XB], xs1[XB], xs2[XB], xs3[STAGES > 3 ? XB : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ws0[WB], ws1[WB], ws2[WB], ws3[STAGES > 3 ? WB : 16];
-    uint8_t* const xs[4] = {xs0, xs1, xs2, xs3};
-    uint8_t* const ws[4] = {ws0, ws1, ws2, ws3};
-
+__global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict__ X,
+                                                      const uint16_t* __restrict__ W, int M, int T,
+                                                      int mtiles, uint16_t* __restrict__ out) {
+    using namespace up;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * SB];
     // Consecutive workgroups sweep the token tiles of one head; XCD x (workgroups are dealt
     // round-robin) then holds token tiles x, x+8, ... for every head in its L2.
     const int h = blockIdx.x / mtiles, mt = blockIdx.x % mtiles;
     const int m0 = mt * BM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % (BM / 64), wn = wave / (BM / 64);
+    const int wm = wave % 4, wn = wave / 4;
 
-    // DMA: a stage is BM/16 one-KB loads of X rows and 16 of W rows; wave w loads X rows
-    // 32w..32w+31 and W rows (16 WLOADS) w.., so every wave has the same count in flight. A 1 KB
-    // load covers 16 rows of 64 bytes; lane i writes row (i >> 2), physical chunk (i & 3), so it
-    // fetches logical chunk (i & 3) ^ ((row >> 2) & 3).
-    int x_src[2], w_src[WLOADS];
+    // DMA: a 1 KB load covers 8 rows of 128 bytes; lane i writes row i / 8, physical chunk i % 8,
+    // i.e. logical chunk (i % 8) ^ key(row). Wave w loads X rows 32w..32w+31 and W rows
+    // 32w..32w+31 (four loads each). X rows past M repeat row M - 1 (never stored).
+    const int pc = lane & 7;
+    uint32_t x_voff[4], w_voff[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int xr = 32 * wave + 16 * j + (lane >> 2);
-        x_src[j] = (min(m0 + xr, M - 1) - m0) * kLora + (((lane & 3) ^ ((xr >> 2) & 3)) * 8);
+    for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        x_voff[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * (kLora * 2) + ((pc ^ key(r)) << 4));
+        w_voff[j] = (uint32_t)(r * (kLora * 2) + ((pc ^ key(r)) << 4));
     }
+    const uint16_t* xg = X + (size_t)m0 * kLora;
+    const uint16_t* wg = W + (size_t)h * BN * kLora;
+    const uint32_t ring_l = lds_addr(ring);
+    auto issue = [&](int kc, int stage) {
+        const uint32_t st = ring_l + stage * SB;
 #pragma unroll
-    for (int j = 0; j < WLOADS; ++j) {
-        const int wr = 16 * WLOADS * wave + 16 * j + (lane >> 2);
-        w_src[j] = wr * kLora + (((lane & 3) ^ ((wr >> 2) & 3)) * 8);
-    }
-    const uint16_t* xbase = X + (size_t)m0 * kLora;
-    const uint16_t* wbase = W + (size_t)h * BN * kLora;
-    auto issue = [&](int kc, uint8_t* xdst, uint8_t* wdst) {
+        for (int j = 0; j < 4; ++j) dma16_lds(xg + kc * BK, x_voff[j], st + (32 * wave + 8 * j) * ROWB);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma16_g(xbase + kc * BK + x_src[j], xdst + (32 * wave + 16 * j) * ROWB);
-#pragma unroll
-        for (int j = 0; j < WLOADS; ++j)
-            dma16_g(wbase + kc * BK + w_src[j], wdst + (16 * WLOADS * wave + 16 * j) * ROWB);
+        for (int j = 0; j < 4; ++j) dma16_lds(wg + kc * BK, w_voff[j], st + XB + (32 * wave + 8 * j) * ROWB);
     };
 
+    // MFMA operand reads: row (l % 32) of a 32-row block, logical chunk 2s + l/32 of k-step s;
+    // block row bases are multiples of 32, so the swizzle key is that of l % 32 alone.
+    const int fr = lane & 31, fh = lane >> 5, fk = key(fr);
+    const int xrow = (wm * 64 + fr) * ROWB, wrow = XB + (wn * 128 + fr) * ROWB;
     f32x16 acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-    // MFMA operand reads: row (l % 32) of a 32-row block, 16-byte chunk (2s + l/32), swizzled.
-    const int fr = lane & 31, fh = lane >> 5;
-    int x_off[2][2], w_off[4][2];   // [block][k-step of 16]
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int row = wm * 64 + b * 32 + fr;
-            x_off[b][s] = row * ROWB + (((2 * s + fh) ^ ((row >> 2) & 3)) << 4);
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int row = wn * 128 + a * 32 + fr;
-            w_off[a][s] = row * ROWB + (((2 * s + fh) ^ ((row >> 2) & 3)) << 4);
-        }
-    }
-
-    // Chunks are issued STAGES-1 ahead; the end of chunk kc waits for chunk kc+1 and leaves
-    // the newer ones in flight.
-    constexpr int NK = kLora / BK;   // 16 chunks
-#pragma unroll
-    for (int c = 0; c < STAGES - 1; ++c) issue(c, xs[c], ws[c]);
-    __builtin_amdgcn_s_waitcnt(0x3F70 | (LOADS * (STAGES - 2)));   // chunk 0 landed
+    issue(0, 0);
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));   // chunk 0 landed
     barrier_keep_loads();
 #pragma unroll
     for (int kc = 0; kc < NK; ++kc) {
-        const int st = kc % STAGES;
-        if (kc + STAGES - 1 < NK) issue(kc + STAGES - 1, xs[(kc + STAGES - 1) % STAGES], ws[(kc + STAGES - 1) % STAGES]);
-        __builtin_amdgcn_sched_barrier(0);       // keep the loads at the top of the chunk
-        const uint8_t* xb = xs[st];
-        const uint8_t* wb = ws[st];
+        const uint8_t* st = ring + (kc & 1) * SB;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < BK / 16; ++s) {
+            const int c = ((2 * s + fh) ^ fk) << 4;
             bf16x8 bx[2], aw[4];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(xb + x_off[b][s]));
+            for (int b = 0; b < 2; ++b) bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + xrow + c + b * 32 * ROWB));
 #pragma unroll
-            for (int a = 0; a < 4; ++a) aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(wb + w_off[a][s]));
+            for (int a = 0; a < 4; ++a) aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + wrow + c + a * 32 * ROWB));
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
         }
-        // chunk kc+1 must have landed; the chunks issued after it may stay in flight
-        {
-            const int newer = min(NK - 1, kc + STAGES - 1) - (kc + 1);
-            if (newer >= 2)
-                __builtin_amdgcn_s_waitcnt(0x3F70 | (LOADS * 2));
-            else if (newer == 1)
-                __builtin_amdgcn_s_waitcnt(0x3F70 | LOADS);
-            else
-                __builtin_amdgcn_s_waitcnt(0x3F70);
-        }
+        // chunk kc + 1 (the only one in flight) has landed and every wave is done with this
+        // stage, which then takes chunk kc + 2
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         barrier_keep_loads();
+        if (kc + 2 < NK) issue(kc + 2, kc & 1);
     }
 
-    // Epilogue: each wave stages one 32-token x 128-feature block at a time in its own 8 KB of
-    // the (now idle) ring, rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
-    // writes it back as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store).
-    // The barrier ending the K loop (after vmcnt(0)) guarantees that no wave still reads the
-    // ring and no load into it is in flight.
-    uint8_t* ot;
-    if (BM == 128) {
-        ot = (wave < 2 ? ws0 : ws1) + (wave & 1) * 8192;
-    } else {
-        const int sl = wave >> 1;                           // 16 KB arrays: two waves each
-        ot = (sl == 0 ? xs0 : sl == 1 ? xs1 : sl == 2 ? xs2 : ws0) + (wave & 1) * 8192;
-    }
+    // Epilogue: wave w stages one 32-token x 128-feature block at a time in ring bytes
+    // [8192 w, 8192 w + 8192), rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
+    // writes it as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store). The
+    // last barrier of the K loop (after vmcnt(0)) guarantees that no wave still reads the ring
+    // and no load into it is in flight.
+    uint8_t* ot = ring + wave * 8192;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -411,10 +358,9 @@ __global__ __launch_bounds__(BM * 2) void gemm_up_kernel(const uint16_t* __restr
 
 hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B, int T, uint16_t* kv,
                              hipStream_t stream) {
-    constexpr int BM = UP_BM;
     const int M = B * T;
-    const int mtiles = (M + BM - 1) / BM;
-    gemm_up_kernel<BM><<<mtiles * kHeads, BM * 2, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
+    const int mtiles = (M + up::BM - 1) / up::BM;
+    gemm_up_kernel<<<mtiles * kHeads, 512, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
     return hipGetLastError();
 }
 
