@@ -329,8 +329,11 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
     // [8192 w, 8192 w + 8192), rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
     // writes it as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store). The
     // last barrier of the K loop (after vmcnt(0)) guarantees that no wave still reads the ring
-    // and no load into it is in flight.
+    // and no load into it is in flight. Token m = b T + t goes to kv row (b * 128 + h) * T + t:
+    // the block's first token is split into (b, t) once, and each later row is 256 elements
+    // further, plus (128 T - T) rows each time the block crosses into the next sequence.
     uint8_t* ot = ring + wave * 8192;
+    const size_t seq_jump = (size_t)(kHeads - 1) * T * 256;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -343,14 +346,25 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
                 const int chunk = (4 * a + g) ^ (fr & 15);
                 *reinterpret_cast<u32x2*>(ot + fr * 256 + chunk * 16 + fh * 8) = v;
             }
+        const int mb = m0 + wm * 64 + b * 32;           // the block's first token (wave-uniform)
+        const int b0 = mb / T, t0 = mb - b0 * T;
+        const int c = lane & 15;
+        uint16_t* const dst0 = out + (((size_t)b0 * kHeads + h) * T + t0) * 256 + wn * 128 + c * 8;
+        u32x4 v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int row = 4 * j + (lane >> 4), c = lane & 15;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
-            const int m = m0 + wm * 64 + b * 32 + row;
-            if (m < M) {
-                const int bb = m / T, t = m - bb * T;
-                store16(out + (((size_t)bb * kHeads + h) * T + t) * 256 + wn * 128 + c * 8, v);
+            const int row = 4 * j + (lane >> 4);
+            v[j] = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+        }
+        if (mb + 32 <= M && t0 + 32 <= T) {   // every row of the block is stored, one sequence
+#pragma unroll
+            for (int j = 0; j < 8; ++j) store16(dst0 + (size_t)(4 * j + (lane >> 4)) * 256, v[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 4 * j + (lane >> 4);
+                if (mb + row < M)
+                    store16(dst0 + (size_t)row * 256 + (size_t)((t0 + row) / T) * seq_jump, v[j]);
             }
         }
     }
