@@ -244,7 +244,10 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
 // piece a load fetches is one whole 128-byte line (32-deep chunks fetched half lines, each line
 // twice, and ran 4% slower). 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16 lanes
 // of an operand read hit 16 distinct bank groups. The epilogue stages each wave's 32 x 128 bf16
-// blocks in its own 8 KB of the idle ring and writes whole 256-byte half rows of kv[b][h][t].
+// blocks in its own 8 KB of the idle stage 1 and writes whole 256-byte half rows of kv[b][h][t].
+// Persistent: one workgroup per compute unit steps through its tiles; the first chunk of its
+// next tile loads into stage 0 during the epilogue and the second right after it, so the tile
+// change costs no load latency and the stores drain under the next tile's MFMAs.
 // ------------------------------------------------------------------------------------------------
 namespace up {
 constexpr int BM = 256, BN = 256, BK = 64, ROWB = BK * 2;
@@ -258,10 +261,7 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
                                                       int mtiles, uint16_t* __restrict__ out) {
     using namespace up;
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * SB];
-    // Consecutive workgroups sweep the token tiles of one head; XCD x (workgroups are dealt
-    // round-robin) then holds token tiles x, x+8, ... for every head in its L2.
-    const int h = blockIdx.x / mtiles, mt = blockIdx.x % mtiles;
-    const int m0 = mt * BM;
+    const int ntot = mtiles * kHeads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % 4, wn = wave / 4;
@@ -270,15 +270,29 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
     // i.e. logical chunk (i % 8) ^ key(row). Wave w loads X rows 32w..32w+31 and W rows
     // 32w..32w+31 (four loads each). X rows past M repeat row M - 1 (never stored).
     const int pc = lane & 7;
-    uint32_t x_voff[4], w_voff[4];
+    uint32_t w_voff[4], x_voff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = 32 * wave + 8 * j + (lane >> 3);
-        x_voff[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * (kLora * 2) + ((pc ^ key(r)) << 4));
         w_voff[j] = (uint32_t)(r * (kLora * 2) + ((pc ^ key(r)) << 4));
     }
-    const uint16_t* xg = X + (size_t)m0 * kLora;
-    const uint16_t* wg = W + (size_t)h * BN * kLora;
+    // Tile id: head id / mtiles, token tile id % mtiles. Workgroup w (on XCD w % 8; the grid is a
+    // multiple of 8) takes ids w, w + G, ...: with mtiles a multiple of 8 each XCD keeps the same
+    // token tiles, which stay in its L2 while the heads go by.
+    int h = 0, m0 = 0;
+    const uint16_t* xg = X;
+    const uint16_t* wg = W;
+    auto set_tile = [&](int id) {
+        h = id / mtiles;
+        m0 = (id - h * mtiles) * BM;
+        xg = X + (size_t)m0 * kLora;
+        wg = W + (size_t)h * BN * kLora;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 32 * wave + 8 * j + (lane >> 3);
+            x_voff[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * (kLora * 2) + ((pc ^ key(r)) << 4));
+        }
+    };
     const uint32_t ring_l = lds_addr(ring);
     auto issue = [&](int kc, int stage) {
         const uint32_t st = ring_l + stage * SB;
@@ -292,81 +306,101 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
     // block row bases are multiples of 32, so the swizzle key is that of l % 32 alone.
     const int fr = lane & 31, fh = lane >> 5, fk = key(fr);
     const int xrow = (wm * 64 + fr) * ROWB, wrow = XB + (wn * 128 + fr) * ROWB;
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    // kv row of token m = b T + t is (b * 128 + h) * T + t: one sequence further is (128 T - T)
+    // rows further than the next position
+    const size_t seq_jump = (size_t)(kHeads - 1) * T * 256;
 
+    int id = blockIdx.x;
+    set_tile(id);
     issue(0, 0);
     issue(1, 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));   // chunk 0 landed
-    barrier_keep_loads();
-#pragma unroll
-    for (int kc = 0; kc < NK; ++kc) {
-        const uint8_t* st = ring + (kc & 1) * SB;
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int c = ((2 * s + fh) ^ fk) << 4;
-            bf16x8 bx[2], aw[4];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + xrow + c + b * 32 * ROWB));
-#pragma unroll
-            for (int a = 0; a < 4; ++a) aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + wrow + c + a * 32 * ROWB));
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
-        }
-        // chunk kc + 1 (the only one in flight) has landed and every wave is done with this
-        // stage, which then takes chunk kc + 2
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        barrier_keep_loads();
-        if (kc + 2 < NK) issue(kc + 2, kc & 1);
-    }
-
-    // Epilogue: wave w stages one 32-token x 128-feature block at a time in ring bytes
-    // [8192 w, 8192 w + 8192), rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
-    // writes it as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store). The
-    // last barrier of the K loop (after vmcnt(0)) guarantees that no wave still reads the ring
-    // and no load into it is in flight. Token m = b T + t goes to kv row (b * 128 + h) * T + t:
-    // the block's first token is split into (b, t) once, and each later row is 256 elements
-    // further, plus (128 T - T) rows each time the block crosses into the next sequence.
-    uint8_t* ot = ring + wave * 8192;
-    const size_t seq_jump = (size_t)(kHeads - 1) * T * 256;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (;;) {
+        f32x16 acc[4][2];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 v;
-                v[0] = pack_bf16(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
-                v[1] = pack_bf16(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
-                const int chunk = (4 * a + g) ^ (fr & 15);
-                *reinterpret_cast<u32x2*>(ot + fr * 256 + chunk * 16 + fh * 8) = v;
+            for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+        // chunk 0 has landed: the loads of a wave complete in issue order and only chunk 1's
+        // eight (and, after the first tile, stores issued before them) may be in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        barrier_keep_loads();
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) {
+            const uint8_t* st = ring + (kc & 1) * SB;
+#pragma unroll
+            for (int s = 0; s < BK / 16; ++s) {
+                const int c = ((2 * s + fh) ^ fk) << 4;
+                bf16x8 bx[2], aw[4];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) bx[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + xrow + c + b * 32 * ROWB));
+#pragma unroll
+                for (int a = 0; a < 4; ++a) aw[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + wrow + c + a * 32 * ROWB));
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
             }
-        const int mb = m0 + wm * 64 + b * 32;           // the block's first token (wave-uniform)
-        const int b0 = mb / T, t0 = mb - b0 * T;
-        const int c = lane & 15;
-        uint16_t* const dst0 = out + (((size_t)b0 * kHeads + h) * T + t0) * 256 + wn * 128 + c * 8;
-        u32x4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 4 * j + (lane >> 4);
-            v[j] = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+            // chunk kc + 1 (the only one in flight) has landed and every wave is done with this
+            // stage, which then takes chunk kc + 2
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            barrier_keep_loads();
+            if (kc + 2 < NK) issue(kc + 2, kc & 1);
         }
-        if (mb + 32 <= M && t0 + 32 <= T) {   // every row of the block is stored, one sequence
+
+        // Both stages are free. Chunk 0 of the workgroup's next tile starts loading into stage 0
+        // now, so it lands under the epilogue; chunk 1 follows into stage 1 once every wave has
+        // read its staged rows.
+        const int cur_m0 = m0, cur_h = h;
+        const int next = id + (int)gridDim.x;
+        const bool more = next < ntot;
+        if (more) {
+            set_tile(next);
+            issue(0, 0);
+        }
+        // Epilogue: wave w stages one 32-token x 128-feature block at a time in stage 1 bytes
+        // [8192 w, 8192 w + 8192), rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
+        // writes it as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store). The
+        // block's first token is split into (sequence, position) once; each later row is 256
+        // elements further, plus one sequence jump per sequence end inside the block.
+        uint8_t* ot = ring + SB + wave * 8192;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) store16(dst0 + (size_t)(4 * j + (lane >> 4)) * 256, v[j]);
-        } else {
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 v;
+                    v[0] = pack_bf16(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
+                    v[1] = pack_bf16(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
+                    const int chunk = (4 * a + g) ^ (fr & 15);
+                    *reinterpret_cast<u32x2*>(ot + fr * 256 + chunk * 16 + fh * 8) = v;
+                }
+            const int mb = cur_m0 + wm * 64 + b * 32;      // the block's first token (wave-uniform)
+            const int b0 = mb / T, t0 = mb - b0 * T;
+            const int c = lane & 15;
+            uint16_t* const dst0 = out + (((size_t)b0 * kHeads + cur_h) * T + t0) * 256 + wn * 128 + c * 8;
+            u32x4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = 4 * j + (lane >> 4);
-                if (mb + row < M)
-                    store16(dst0 + (size_t)row * 256 + (size_t)((t0 + row) / T) * seq_jump, v[j]);
+                v[j] = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+            }
+            if (mb + 32 <= M && t0 + 32 <= T) {   // every row of the block is stored, one sequence
+#pragma unroll
+                for (int j = 0; j < 8; ++j) store16(dst0 + (size_t)(4 * j + (lane >> 4)) * 256, v[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int row = 4 * j + (lane >> 4);
+                    if (mb + row < M)
+                        store16(dst0 + (size_t)row * 256 + (size_t)((t0 + row) / T) * seq_jump, v[j]);
+                }
             }
         }
+        if (!more) break;
+        barrier_keep_loads();   // every wave has read its staged rows out of stage 1
+        issue(1, 1);
+        id = next;
     }
 }
 
@@ -374,7 +408,15 @@ hipError_t launch_gemm_kv_up(const uint16_t* c_kv, const uint16_t* w_ukv, int B,
                              hipStream_t stream) {
     const int M = B * T;
     const int mtiles = (M + up::BM - 1) / up::BM;
-    gemm_up_kernel<<<mtiles * kHeads, 512, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
+    const int ntot = mtiles * kHeads;                   // a multiple of 8
+    // one workgroup per compute unit (its LDS admits one), a multiple of 8
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n >= 8) cus = n;
+    }
+    const int G = min(ntot, cus / 8 * 8);
+    gemm_up_kernel<<<G, 512, 0, stream>>>(c_kv, w_ukv, M, T, mtiles, kv);
     return hipGetLastError();
 }
 
