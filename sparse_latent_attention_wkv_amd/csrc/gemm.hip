@@ -244,10 +244,11 @@ hipError_t launch_gemm_kv_down(const uint16_t* x, const uint16_t* w_dkv, int M, 
 // piece a load fetches is one whole 128-byte line (32-deep chunks fetched half lines, each line
 // twice, and ran 4% slower). 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16 lanes
 // of an operand read hit 16 distinct bank groups. The epilogue stages each wave's 32 x 128 bf16
-// blocks in its own 8 KB of the idle stage 1 and writes whole 256-byte half rows of kv[b][h][t].
-// Persistent: one workgroup per compute unit steps through its tiles; the first chunk of its
-// next tile loads into stage 0 during the epilogue and the second right after it, so the tile
-// change costs no load latency and the stores drain under the next tile's MFMAs.
+// blocks in the 8 KB of stage 1 that its own loads fill, and writes whole 256-byte half rows of
+// kv[b][h][t]. Persistent: one workgroup per compute unit steps through its tiles; chunk 0 of its
+// next tile loads into stage 0 during the last chunk and the epilogue, and each wave loads its
+// part of chunk 1 as soon as it has stored its own rows, so the tile change costs no load latency
+// and the stores drain under the next tile's MFMAs.
 // ------------------------------------------------------------------------------------------------
 namespace up {
 constexpr int BM = 256, BN = 256, BK = 64, ROWB = BK * 2;
@@ -315,6 +316,9 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
     issue(0, 0);
     issue(1, 1);
     for (;;) {
+        const int cur_m0 = m0, cur_h = h;
+        const int next = id + (int)gridDim.x;
+        const bool more = next < ntot;
         f32x16 acc[4][2];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -340,29 +344,29 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
 #pragma unroll
                     for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(aw[a], bx[b], acc[a][b]);
             }
-            // chunk kc + 1 (the only one in flight) has landed and every wave is done with this
-            // stage, which then takes chunk kc + 2
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            barrier_keep_loads();
-            if (kc + 2 < NK) issue(kc + 2, kc & 1);
+            if (kc + 1 < NK) {
+                // chunk kc + 1 (the only one of this tile in flight) has landed and every wave is
+                // done with this stage, which then takes chunk kc + 2, or after the next-to-last
+                // chunk, chunk 0 of the workgroup's next tile
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                barrier_keep_loads();
+                if (kc + 2 < NK) {
+                    issue(kc + 2, kc & 1);
+                } else if (more) {
+                    set_tile(next);
+                    issue(0, 0);
+                }
+            } else {
+                barrier_keep_loads();   // every wave is done with stage 1
+            }
         }
-
-        // Both stages are free. Chunk 0 of the workgroup's next tile starts loading into stage 0
-        // now, so it lands under the epilogue; chunk 1 follows into stage 1 once every wave has
-        // read its staged rows.
-        const int cur_m0 = m0, cur_h = h;
-        const int next = id + (int)gridDim.x;
-        const bool more = next < ntot;
-        if (more) {
-            set_tile(next);
-            issue(0, 0);
-        }
-        // Epilogue: wave w stages one 32-token x 128-feature block at a time in stage 1 bytes
-        // [8192 w, 8192 w + 8192), rows of 256 bytes with 16-byte chunk c at c ^ (row & 15), then
+        // Epilogue: wave w stages one 32-token x 128-feature block at a time in the stage-1 bytes
+        // its own loads fill (rows 0-15 at 4096 w, rows 16-31 at XB + 4096 w), rows of 256 bytes
+        // with 16-byte chunk c at c ^ (row & 15), then
         // writes it as whole 256-byte half rows of kv (16 bytes per lane, 4 rows per store). The
         // block's first token is split into (sequence, position) once; each later row is 256
         // elements further, plus one sequence jump per sequence end inside the block.
-        uint8_t* ot = ring + SB + wave * 8192;
+        uint8_t* ot = ring + SB + wave * 4096;   // rows 0-15; rows 16-31 at XB further
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
                     v[0] = pack_bf16(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1]);
                     v[1] = pack_bf16(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
                     const int chunk = (4 * a + g) ^ (fr & 15);
-                    *reinterpret_cast<u32x2*>(ot + fr * 256 + chunk * 16 + fh * 8) = v;
+                    *reinterpret_cast<u32x2*>(ot + (fr & 15) * 256 + (fr >> 4) * XB + chunk * 16 + fh * 8) = v;
                 }
             const int mb = cur_m0 + wm * 64 + b * 32;      // the block's first token (wave-uniform)
             const int b0 = mb / T, t0 = mb - b0 * T;
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = 4 * j + (lane >> 4);
-                v[j] = *reinterpret_cast<const u32x4*>(ot + row * 256 + ((c ^ (row & 15)) << 4));
+                v[j] = *reinterpret_cast<const u32x4*>(ot + (row & 15) * 256 + (row >> 4) * XB + ((c ^ (row & 15)) << 4));
             }
             if (mb + 32 <= M && t0 + 32 <= T) {   // every row of the block is stored, one sequence
 #pragma unroll
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
             }
         }
         if (!more) break;
-        barrier_keep_loads();   // every wave has read its staged rows out of stage 1
+        // the wave's staged rows are exactly the stage-1 rows its own loads fill
         issue(1, 1);
         id = next;
     }
