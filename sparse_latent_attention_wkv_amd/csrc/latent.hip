@@ -51,37 +51,50 @@ __device__ __forceinline__ float lane_pair_sum(float v) {
 // ------------------------------------------------------------------------------------------------
 int latent_list_stride(int T, int K) { return (min(T, K) + 63) / 64 * 64; }
 
-// QR query rows per workgroup: their allowed sets as bitmap rows in LDS (the same set semantics
-// as the dense mask), then one wave per row turns its bitmap into the ascending list. Rows
+// QR = 4 query rows per workgroup (one per wave): the wave sets its rows' allowed keys as bits in LDS
+// (the same set semantics as the dense mask), then turns each bitmap row into the ascending list
+// 2048 keys at a time: lane l counts the keys of word l of the batch, a wave-wide prefix count
+// places them in the wave's LDS buffer, and the batch leaves as consecutive 4-byte stores. Rows
 // s_lo..T-1 of each sequence; row s of sequence b is output row b*(T - s_lo) + s - s_lo.
 template <int QR>
 __global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict__ topk, int T, int K, int s_lo,
-                                                       int Lp, int32_t* __restrict__ lists,
+                                                       int Lp, bool vec4, int32_t* __restrict__ lists,
                                                        int32_t* __restrict__ counts) {
+    static_assert(QR == 4, "one row per wave");
     extern __shared__ uint32_t bits_lds[];
     const int Wd = (T + 31) / 32, WP = Wd + 1;
+    uint32_t* const stage_all = bits_lds + QR * WP;   // 4 waves x 2048 entries
     const int Tr = T - s_lo;
     const int s0 = s_lo + blockIdx.x * QR, b = blockIdx.y;
-    const int nrows = max(0, min(QR, T - s0));
-    for (int i = threadIdx.x; i < QR * WP; i += 256) bits_lds[i] = 0;
-    __syncthreads();
-    const int32_t* base = topk + ((size_t)b * T + s0) * K;
-    const int n = nrows * K;
-#pragma unroll 4
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const int t = base[i];
-        const int qi = i / K;
-        if ((unsigned)t <= (unsigned)(s0 + qi)) atomicOr(bits_lds + qi * WP + (t >> 5), 1u << (t & 31));
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int qi = wave; qi < nrows; qi += 4) {
-        const int s = s0 + qi;
-        const uint32_t* row = bits_lds + qi * WP;
+    uint32_t* const stage = stage_all + wave * 2048;
+    {
+        const int qi = wave, s = s0 + qi;
+        if (s >= T) return;
+        uint32_t* row = bits_lds + qi * WP;
+        const int nw = (s >> 5) + 1;             // words that can hold keys <= s
+        for (int w = lane; w < nw; w += 64) row[w] = 0u;
+        // the row's entries; only this wave touches the row, and LDS operations of a wave
+        // complete in order, so the clears land before the first bit is set
+        __builtin_amdgcn_wave_barrier();
+        const int32_t* src = topk + ((size_t)b * T + s) * K;
+        if (vec4) {
+            for (int i = lane; i < K / 4; i += 64) {
+                const int4 v = reinterpret_cast<const int4*>(src)[i];
+                if ((unsigned)v.x <= (unsigned)s) atomicOr(row + (v.x >> 5), 1u << (v.x & 31));
+                if ((unsigned)v.y <= (unsigned)s) atomicOr(row + (v.y >> 5), 1u << (v.y & 31));
+                if ((unsigned)v.z <= (unsigned)s) atomicOr(row + (v.z >> 5), 1u << (v.z & 31));
+                if ((unsigned)v.w <= (unsigned)s) atomicOr(row + (v.w >> 5), 1u << (v.w & 31));
+            }
+        } else {
+            for (int i = lane; i < K; i += 64) {
+                const int t = src[i];
+                if ((unsigned)t <= (unsigned)s) atomicOr(row + (t >> 5), 1u << (t & 31));
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
         const size_t orow = (size_t)b * Tr + (s - s_lo);
         int32_t* dst = lists + orow * Lp;
-        const int nw = (s >> 5) + 1;             // words that can hold keys <= s
         int total = 0;
         for (int c = 0; c < nw; c += 64) {
             const int w = c + lane;
@@ -93,12 +106,16 @@ __global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict
                 const int t = __shfl_up(incl, off, 64);
                 if (lane >= off) incl += t;
             }
-            int pos = total + incl - pc;
+            int pos = incl - pc;
             while (word) {
-                dst[pos++] = (w << 5) + (__ffs(word) - 1);
+                stage[pos++] = (uint32_t)((w << 5) + (__ffs(word) - 1));
                 word &= word - 1;
             }
-            total += __shfl(incl, 63, 64);
+            const int n = __shfl(incl, 63, 64);
+            __builtin_amdgcn_wave_barrier();
+            for (int p = lane; p < n; p += 64) dst[total + p] = (int32_t)stage[p];
+            __builtin_amdgcn_wave_barrier();
+            total += n;
         }
         const int padded = (total + 63) & ~63;
         for (int p = total + lane; p < padded; p += 64) dst[p] = 0;
@@ -108,10 +125,11 @@ __global__ __launch_bounds__(256) void sel_list_kernel(const int32_t* __restrict
 
 static hipError_t launch_sel_list_range(const int32_t* topk, int B, int T, int K, int s_lo, int32_t* lists,
                                         int32_t* counts, hipStream_t stream) {
-    constexpr int QR = 8;
+    constexpr int QR = 4;
     const dim3 grid((T - s_lo + QR - 1) / QR, B);
-    const size_t lds = (size_t)QR * ((T + 31) / 32 + 1) * sizeof(uint32_t);
-    sel_list_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, s_lo, latent_list_stride(T, K), lists, counts);
+    const size_t lds = ((size_t)QR * ((T + 31) / 32 + 1) + 4 * 2048) * sizeof(uint32_t);
+    const bool vec4 = (K & 3) == 0 && ((uintptr_t)topk & 15) == 0;
+    sel_list_kernel<QR><<<grid, 256, lds, stream>>>(topk, T, K, s_lo, latent_list_stride(T, K), vec4, lists, counts);
     return hipGetLastError();
 }
 
