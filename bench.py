@@ -441,24 +441,28 @@ def main():
     scale = mla.mla_default_softmax_scale()
     stream = torch.cuda.current_stream(dev)
     # Head-major path: the selection bitmap depends only on the top-k indices, so it is built on a
-    # second stream (default priority) while the up-projection runs (measured in one process:
-    # 1.880 ms per step against 1.897 ms sequentially; from the step's start, concurrent with the
-    # down-projection, it gained nothing). The second stream first waits for the main stream, so
-    # the previous step's attention, which reads the same workspace, has finished.
+    # second stream (default priority) from the step's start, on the compute units the
+    # down-projection (192 workgroups) leaves free and beside the up-projection (measured in one
+    # process: 1.898 ms per step against 1.904 ms when it starts after the down-projection; both
+    # faster than sequential). The second stream first waits for the main stream, so the previous
+    # step's attention, which reads the same workspace, has finished.
     side = torch.cuda.Stream(dev)
     sync_start, sync_ready = torch.cuda.Event(), torch.cuda.Event()
 
-    def step(ev=None):
+    def step(ev=None, split=False):
+        # ev: timing events at the step's start, before the attention and at the step's end;
+        # split: one more between the down- and up-projections (kept out of the timed steps)
         if ev is not None:
             ev[0].record(stream)
-        mla.mla_kv_latent(x, w_dkv, gain, 1e-6, rope_cs, out=(kv_raw, c_kv, k_pe))
-        if ev is not None:
-            ev[1].record(stream)
         if kv is not None:
             sync_start.record(stream)
             side.wait_event(sync_start)
             mla.mla_attn_prepare(topk, ws, stream=side)
             sync_ready.record(side)
+        mla.mla_kv_latent(x, w_dkv, gain, 1e-6, rope_cs, out=(kv_raw, c_kv, k_pe))
+        if split:
+            ev[1].record(stream)
+        if kv is not None:
             mla.mla_kv_up(c_kv, w_ukv, out=kv)
         if ev is not None:
             ev[2].record(stream)
@@ -491,11 +495,16 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    lat = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    upm = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     att = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
+    # the split of the first part of the step into its two calls, from a few more (untimed) steps
+    evs_split = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(min(args.steps, 10))]
+    for e in evs_split:
+        step(e, split=True)
+    torch.cuda.synchronize()
+    lat = np.mean([e[0].elapsed_time(e[1]) for e in evs_split])
+    upm = np.mean([e[1].elapsed_time(e[2]) for e in evs_split])
 
     clock_mhz = None
     if kv is not None and not args.no_clock_sample:
