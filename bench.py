@@ -358,9 +358,9 @@ def query_path_measurement(torch, mla, dev, stream, B: int, T: int) -> dict:
     return {"tokens": M, "us": us, "TFLOP_s": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS, "flop": flop}
 
 
-def mfma_busy_record():
-    """MFMA-busy fraction of the attention kernel from a rocprofv3 counter run, if the record
-    matches the current kernel source (else None)."""
+def attn_counter_record(key: str):
+    """A figure of the attention kernel's rocprofv3 counter record (profiles/sparse_attn_traffic.txt),
+    if the record matches the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "sparse_attn_traffic.txt")
     src = os.path.join(ROOT, "sparse_latent_attention_wkv_amd", "csrc", "attn.hip")
     if not os.path.exists(path) or not os.path.exists(src):
@@ -371,9 +371,31 @@ def mfma_busy_record():
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("source_sha") != sha or "mfma_busy_frac" not in kv:
+    if kv.get("source_sha") != sha or key not in kv:
         return None
-    return float(kv["mfma_busy_frac"])
+    return float(kv[key])
+
+
+def mfma_busy_record():
+    """MFMA-busy fraction of the attention kernel from a rocprofv3 counter run, or None."""
+    return attn_counter_record("mfma_busy_frac")
+
+
+# An engine clock read while the attention runs is taken only inside this range (MHz): the
+# kernel keeps the matrix units about half busy, and its counters put the clock near 1.9 GHz.
+CLOCK_PLAUSIBLE_MHZ = (1000.0, 2600.0)
+
+
+def attention_clock(sampled):
+    """(clock MHz, source): the sampled engine clock if plausible, else the clock from the counter
+    record (GRBM_GUI_ACTIVE per XCD over the kernel's duration), else (None, None)."""
+    if sampled is not None and CLOCK_PLAUSIBLE_MHZ[0] <= sampled <= CLOCK_PLAUSIBLE_MHZ[1]:
+        return sampled, "amdsmi current_gfxclk, median while the attention runs"
+    rec = attn_counter_record("gfx_clock_mhz")
+    if rec is not None:
+        why = "no amdsmi reading" if sampled is None else f"amdsmi read {sampled:.0f} MHz, outside {CLOCK_PLAUSIBLE_MHZ}"
+        return rec, f"rocprofv3 counters (profiles/sparse_attn_traffic.txt); {why}"
+    return None, None
 
 
 def main():
@@ -506,11 +528,17 @@ def main():
     lat = np.mean([e[0].elapsed_time(e[1]) for e in evs_split])
     upm = np.mean([e[1].elapsed_time(e[2]) for e in evs_split])
 
-    clock_mhz = None
-    if kv is not None and not args.no_clock_sample:
-        stream.wait_event(sync_ready)
-        clock_mhz = sample_gfx_clock(torch, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale,
-                                                                                         out=out), 400)
+    clock_mhz, clock_src = None, None
+    if kv is not None:
+        sampled = None
+        if not args.no_clock_sample:
+            stream.wait_event(sync_ready)
+            sampled = sample_gfx_clock(torch, lambda: mla.mla_sparse_prefill_attn_prepared(q, kv, k_pe, ws, scale,
+                                                                                           out=out), 400)
+        if args.workload == "headline" and args.path == "head-major":
+            clock_mhz, clock_src = attention_clock(sampled)
+        elif sampled is not None and CLOCK_PLAUSIBLE_MHZ[0] <= sampled <= CLOCK_PLAUSIBLE_MHZ[1]:
+            clock_mhz, clock_src = sampled, "amdsmi current_gfxclk, median while the attention runs"
 
     window = None
     if kv is not None:
@@ -571,6 +599,7 @@ def main():
                      "scored_tiles": None if tiles is None else int(tiles.sum()),
                      "causal_tiles": B * causal_tiles(T),
                      "measured_gfx_clock_mhz": clock_mhz,
+                     "clock_source": clock_src,
                      "peak_at_measured_clock": None if clock_mhz is None else PEAK_BF16_TFLOPS * clock_mhz / 2400.0,
                      "frac_at_measured_clock": (None if clock_mhz is None else
                                                 achieved / (PEAK_BF16_TFLOPS * clock_mhz / 2400.0))},

@@ -69,3 +69,16 @@ def test_flagged_tiles_against_the_oracle_mask():
         assert np.array_equal(bench.flagged_tiles(topk), want)
     assert bench.flagged_tiles(np.full((1, 10, 4), -1, np.int32)).tolist() == [[1]]
     assert bench.causal_tiles(64) == 1 and bench.causal_tiles(65) == 2 and bench.causal_tiles(300) == 4 + 5
+
+
+def test_attention_clock_falls_back_to_the_counter_record():
+    """An amdsmi engine-clock sample outside the plausible range under load (an idle or
+    per-partition reading) is replaced by the clock from the kernel's counter record, which
+    matches the current kernel source."""
+    rec = bench.attn_counter_record("gfx_clock_mhz")
+    assert rec is not None and 1000 <= rec <= 2600
+    assert bench.attention_clock(1950.0) == (1950.0, bench.attention_clock(1950.0)[1])
+    assert "amdsmi" in bench.attention_clock(1950.0)[1]
+    for bad in (None, 660.0, 9000.0):
+        clk, src = bench.attention_clock(bad)
+        assert clk == rec and "counters" in src
