@@ -133,10 +133,12 @@ def _check_up(c_rows, w, got):       # c_rows [n, 512], got [n, 128, 256]
     assert (np.abs(got - ref) <= bf16_step(ref)).mean() >= 0.999
 
 
-@pytest.mark.parametrize("B,T", [(1, 64), (2, 77), (1, 1024), (3, 5), (9, 33)])
+@pytest.mark.parametrize("B,T", [(1, 64), (2, 77), (1, 1024), (3, 5), (9, 33), (3, 700)])
 def test_kv_up(B, T):
     """(3, 5) and (9, 33): sequences shorter than a 32-token output block, and blocks that
-    cross one sequence boundary, so the epilogue's row-to-(sequence, position) stepping is used."""
+    cross one sequence boundary, so the epilogue's row-to-(sequence, position) stepping is used.
+    (1, 1024) and (3, 700): several tiles per persistent workgroup, the latter with a ragged last
+    token tile (2100 tokens), so the next tile's loads overlap an epilogue."""
     say(f"kv_up B={B} T={T}")
     c = bf(3000 + T, (B, T, 512))
     w = synth.make("tiny", ("w_ukv",))["w_ukv"]
