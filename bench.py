@@ -322,6 +322,26 @@ def side_measurements(torch, mla, dev, stream, topk, B: int, T: int, K: int) -> 
     us_w = timed_us(torch, stream, lambda: L.mla_window_kv(*wargs), reps=200, warm=20)
     w_bytes = 3072.0 * 256
     window = {"rows": 256, "us": us_w, "GB_s": w_bytes / (us_w * 1e-6) / 1e9, "bytes": w_bytes}
+    # The same decode step at 64 consecutive positions, captured once in a HIP graph (one eager
+    # pass on the capture stream first) and replayed: no host launch per step.
+    steps = 64
+    gcs = mla.mla_rope_table(1000 + steps, dev)
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for i in range(steps):
+            mla.mla_window_kv(wraw, gain, wcache, start_pos=1000 + i, rope_cs=gcs, out=(wout,))
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(steps):
+            mla.mla_window_kv(wraw, gain, wcache, start_pos=1000 + i, rope_cs=gcs, out=(wout,))
+    torch.cuda.synchronize()
+    us_g = timed_us(torch, stream, graph.replay, reps=20, warm=3) / steps
+    window.update({"graph_steps": steps, "graph_us_per_step": us_g,
+                   "graph_GB_s": w_bytes / (us_g * 1e-6) / 1e9})
+    del graph
     del kv_raw, c_kv, k_pe, bm, kc, pc, wraw, wcache, wout
     # The front-end workload's decode variant: 256 rows of 512, RMSNorm eps 1e-20, no rotary
     # (1024 B read + 1024 B written per row; launch-bound), through the C entry point.
