@@ -277,9 +277,9 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
         const int r = 32 * wave + 8 * j + (lane >> 3);
         w_voff[j] = (uint32_t)(r * (kLora * 2) + ((pc ^ key(r)) << 4));
     }
-    // Tile id: head id / mtiles, token tile id % mtiles. Workgroup w (on XCD w % 8; the grid is a
-    // multiple of 8) takes ids w, w + G, ...: with mtiles a multiple of 8 each XCD keeps the same
-    // token tiles, which stay in its L2 while the heads go by.
+    // Tile id: head id / mtiles, token tile id % mtiles. Workgroup w (on XCD w % 8; the grid G is
+    // a multiple of 8) takes ids w, w + G, ...: with mtiles a multiple of 8, XCD x only ever sees
+    // the token tiles mt = x (mod 8), which stay in its L2 while the heads go by.
     int h = 0, m0 = 0;
     const uint16_t* xg = X;
     const uint16_t* wg = W;
@@ -324,8 +324,9 @@ __global__ __launch_bounds__(512) void gemm_up_kernel(const uint16_t* __restrict
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-        // chunk 0 has landed: the loads of a wave complete in issue order and only chunk 1's
-        // eight (and, after the first tile, stores issued before them) may be in flight
+        // chunk 0 has landed: at most eight of this wave's memory operations remain in flight,
+        // and as its loads complete in issue order and the eight of chunk 1 were issued after
+        // those of chunk 0, none of chunk 0's can be among them
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
         barrier_keep_loads();
 #pragma unroll
