@@ -16,9 +16,12 @@
 // bank sweep, CPR chunks per row), so the 16 lanes of an operand read hit distinct bank groups. Within a chunk the operands of k-step s + 1 are read
 // before the MFMAs of step s; the one barrier per chunk sits before the last step, after which
 // the freed stage is refilled with the chunk STAGES ahead. The
-// epilogue stages the bf16 tile in the idle ring and writes 16-byte pieces of whole rows. ROPE:
+// epilogue stages the bf16 tile in the idle ring and writes 16-byte pieces of whole rows; its
+// barriers wait for LDS work only, so the stores drain under the next tile's first loads. ROPE:
 // features 128..191 of each 192-wide query head are rotated there, after the bf16 rounding of the
-// product, at position start_pos + (row % T) (the query path's rotary step).
+// product, at position start_pos + (row % T) (the query path's rotary step); the tile's (cos, sin)
+// table rows are loaded into the ring before any store is issued and the tile is staged in two
+// halves, so no wait in the store loop covers the stores already issued.
 //
 // Tile order: tile slot w goes to XCD w mod 8 (workgroups are dealt to the 8 XCDs round-robin,
 // and a persistent workgroup keeps its XCD, stepping through slots by the grid size, a multiple
@@ -179,45 +182,83 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
 
     // Epilogue: every ring read completed before the last barrier and no load is in flight.
     // Tile row r (token) takes BN * 2 bytes; piece c (features 8c..8c+7) sits at c ^ (r & 7).
+    auto stage_rows = [&](int rbase) {   // this wave's rows, at rows - rbase of the ring
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int row = wm * 128 + b * 32 + fr;
+        for (int b = 0; b < 4; ++b) {
+            const int row = wm * 128 + b * 32 + fr - rbase;
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+            for (int a = 0; a < NA; ++a)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x2 v;
-                v[0] = pack_bf16(acc[a][b][4 * q + 0], acc[a][b][4 * q + 1]);
-                v[1] = pack_bf16(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-                const int c = wn * (BN / 16) + 4 * a + q;
-                *reinterpret_cast<u32x2*>(ring + row * (BN * 2) + ((c ^ (row & 7)) << 4) + fh * 8) = v;
-            }
-    }
-    __syncthreads();
-    constexpr int NC = BM * PR / 256;   // pieces per thread
-#pragma unroll 4
-    for (int i = 0; i < NC; ++i) {
-        const int id = i * 256 + tid, row = id / PR, c = id - row * PR;
-        u32x4 v = *reinterpret_cast<const u32x4*>(ring + row * (BN * 2) + ((c ^ (row & 7)) << 4));
-        if (m0 + row >= M) continue;
-        if (ROPE) {
-            const int f = (n0 + 8 * c) % kQkHead;    // feature of this piece within its head
-            if (f >= kNope) {
-                const int pos = start_pos + (m0 + row) % T;
-                const f32x4* cs = reinterpret_cast<const f32x4*>(rope_cs + ((size_t)pos * 32 + (f - kNope) / 2) * 2);
-                const f32x4 cs0 = cs[0], cs1 = cs[1];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float re = bf16lo(v[p]), im = bf16hi(v[p]);
-                    const float cq = p < 2 ? cs0[2 * p] : cs1[2 * p - 4];
-                    const float sq = p < 2 ? cs0[2 * p + 1] : cs1[2 * p - 3];
-                    v[p] = pack_bf16(re * cq - im * sq, re * sq + im * cq);
+                for (int q = 0; q < 4; ++q) {
+                    u32x2 v;
+                    v[0] = pack_bf16(acc[a][b][4 * q + 0], acc[a][b][4 * q + 1]);
+                    v[1] = pack_bf16(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+                    const int c = wn * (BN / 16) + 4 * a + q;
+                    *reinterpret_cast<u32x2*>(ring + row * (BN * 2) + ((c ^ (row & 7)) << 4) + fh * 8) = v;
                 }
+        }
+    };
+    if constexpr (ROPE) {
+        // The (cos, sin) rows of the tile's 256 positions go to the upper half of the ring before
+        // any store is issued; the tile is then staged and stored in two halves of 128 rows, so the
+        // store loop reads only LDS and waits for no memory operation (vector memory waits count
+        // stores too). Thread t stores piece column c = t % PR of rows r0 + 8 i of each half.
+        constexpr int HB = (BM / 2) * (BN * 2);
+        static_assert(PR == 32 && HB + BM * 256 <= STAGES * SB, "half staging plus table rows");
+        {
+            const int step4 = 4 % T;
+            int qr = (m0 + wave * 64 + (lane >> 4)) % T;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {   // 64 rows per wave, 4 rows of 256 bytes per load
+                dma16_lds(rope_cs, (uint32_t)(start_pos + qr) * 256u + (uint32_t)(lane & 15) * 16u,
+                          ring_lds + HB + (uint32_t)(wave * 64 + 4 * k) * 256u);
+                qr += step4;
+                if (qr >= T) qr -= T;
             }
         }
-        store16(out + (size_t)(m0 + row) * ND + n0 + c * 8, v);
+        const int c = tid % PR, r0 = tid / PR;
+        const int f = (n0 + 8 * c) % kQkHead;          // feature of this column within its head
+        const bool rot = f >= kNope;
+        const int jb = rot ? (f - kNope) / 2 : 0;      // first rotary pair of the piece
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) stage_rows(h * 128);
+            if (h == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the table rows (no store of this tile is in flight yet)
+            barrier_keep_loads();
+#pragma unroll 4
+            for (int i = 0; i < 16; ++i) {
+                const int lr = r0 + 8 * i, row = h * 128 + lr;
+                u32x4 v = *reinterpret_cast<const u32x4*>(ring + lr * (BN * 2) + ((c ^ (lr & 7)) << 4));
+                if (rot) {
+                    const f32x4* cs = reinterpret_cast<const f32x4*>(ring + HB + row * 256 + jb * 8);
+                    const f32x4 cs0 = cs[0], cs1 = cs[1];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float re = bf16lo(v[p]), im = bf16hi(v[p]);
+                        const float cq = p < 2 ? cs0[2 * p] : cs1[2 * p - 4];
+                        const float sq = p < 2 ? cs0[2 * p + 1] : cs1[2 * p - 3];
+                        v[p] = pack_bf16(re * cq - im * sq, re * sq + im * cq);
+                    }
+                }
+                if (m0 + row < M) store16(out + (size_t)(m0 + row) * ND + n0 + c * 8, v);
+            }
+            // the staged rows are read before the next half is staged or the next tile's loads
+            // land; the stores drain meanwhile
+            barrier_keep_loads();
+        }
+    } else {
+        stage_rows(0);
+        barrier_keep_loads();
+        constexpr int NC = BM * PR / 256;   // pieces per thread
+#pragma unroll 4
+        for (int i = 0; i < NC; ++i) {
+            const int id = i * 256 + tid, row = id / PR, c = id - row * PR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ring + row * (BN * 2) + ((c ^ (row & 7)) << 4));
+            if (m0 + row < M) store16(out + (size_t)(m0 + row) * ND + n0 + c * 8, v);
+        }
+        // the staging reads are done before the next tile's loads land; the stores drain
+        barrier_keep_loads();
     }
-    __syncthreads();   // the ring's staging reads are done before the next tile's loads land
     }
 }
 
