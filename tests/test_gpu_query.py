@@ -56,7 +56,7 @@ def _check_rows(x, w_qa, gain, w_qb, qa, qr, q, rows_bt, sp):
                                what=f"q_pe[{b},{t}]")
 
 
-CASES = [(1, 64, 0), (2, 77, 13), (1, 1, 0), (1, 300, 4000), (3, 130, 0)]
+CASES = [(1, 64, 0), (2, 77, 13), (1, 1, 0), (1, 3, 5), (2, 150, 2), (1, 300, 4000), (3, 130, 0)]
 
 
 @pytest.mark.parametrize("B,T,sp", CASES)
